@@ -1,0 +1,158 @@
+"""CPU oracle for C = alpha*A*B + beta*C, used as test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never loads it and the
+two share no code: this module wraps ``oracle_gemm.c`` (plain C, fp64
+accumulation, built with gcc) through ctypes.
+
+The definition it follows is the GEMM formula of page "Naive GEMM and
+Roofline analysis", section 10.1, with the row-major indexing of that page's
+naive kernel (section 10.2).  Every function returns the fp64 result together
+with the parity denominator ``|alpha| * sum_k |A*B| + |beta*C_in| + 1e-30``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle_gemm.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+def compile_library(src: str, out: str) -> str:
+    """gcc -O2 -fopenmp: plain IEEE fp64 (no -ffast-math)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Werror", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle_gemm.c into oracle/liboracle.so."""
+    if force or not os.path.exists(LIB_PATH):
+        compile_library(SOURCE, LIB_PATH)
+    return LIB_PATH
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, f64, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        for name in ("oracle_gemm_f32", "oracle_gemm_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [i64, i64, i64, f64, f64, vp, vp, vp, vp, vp]
+            fn.restype = ctypes.c_int
+        for name in ("oracle_gemm_f32_entries", "oracle_gemm_bf16_entries"):
+            fn = getattr(lib, name)
+            fn.argtypes = [i64, i64, i64, f64, f64, vp, vp, vp, i64, vp, vp, vp, vp]
+            fn.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    @staticmethod
+    def _operands(A, B, C, beta, bf16):
+        want = np.uint16 if bf16 else np.float32
+        A = np.ascontiguousarray(A)
+        B = np.ascontiguousarray(B)
+        if A.dtype != want or B.dtype != want:
+            raise TypeError("A and B must be %s arrays" % np.dtype(want).name)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
+            raise ValueError("shapes do not chain: %s x %s" % (A.shape, B.shape))
+        M, K = A.shape
+        N = B.shape[1]
+        if beta != 0.0:
+            if C is None:
+                raise ValueError("beta != 0 needs C_in")
+            C = np.ascontiguousarray(C, dtype=np.float32)
+            if C.shape != (M, N):
+                raise ValueError("C_in must be %dx%d" % (M, N))
+        else:
+            C = None  # never read when beta == 0
+        return A, B, C, M, N, K
+
+    def gemm(self, A, B, C=None, alpha=1.0, beta=0.0, bf16=False):
+        """Full fp64 reference: (C_ref, den), both float64 M x N arrays.
+
+        ``bf16=True``: A and B are uint16 arrays of bf16 bit patterns,
+        otherwise float32.  C is float32 and is read only when beta != 0.
+        """
+        A, B, C, M, N, K = self._operands(A, B, C, beta, bf16)
+        Cref = np.empty((M, N), dtype=np.float64)
+        den = np.empty((M, N), dtype=np.float64)
+        fn = self.lib.oracle_gemm_bf16 if bf16 else self.lib.oracle_gemm_f32
+        rc = fn(M, N, K, float(alpha), float(beta), _ptr(A), _ptr(B), _ptr(C),
+                _ptr(Cref), _ptr(den))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (code %d)" % rc)
+        return Cref, den
+
+    def gemm_entries(self, A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False):
+        """fp64 reference at the sampled positions (rows[e], cols[e]) only."""
+        A, B, C, M, N, K = self._operands(A, B, C, beta, bf16)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.shape != cols.shape or rows.ndim != 1:
+            raise ValueError("rows and cols must be 1-D and of equal length")
+        out = np.empty(rows.shape[0], dtype=np.float64)
+        den = np.empty(rows.shape[0], dtype=np.float64)
+        fn = self.lib.oracle_gemm_bf16_entries if bf16 else self.lib.oracle_gemm_f32_entries
+        rc = fn(M, N, K, float(alpha), float(beta), _ptr(A), _ptr(B), _ptr(C),
+                rows.shape[0], _ptr(rows), _ptr(cols), _ptr(out), _ptr(den))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (code %d)" % rc)
+        return out, den
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=False)
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, bf16=False):
+    return default().gemm(A, B, C, alpha, beta, bf16)
+
+
+def gemm_entries(A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False):
+    return default().gemm_entries(A, B, rows, cols, C, alpha, beta, bf16)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use in this process."""
+    return default().num_threads()
+
+
+def parity_error(c_gpu, c_ref, den) -> float:
+    """max |c - c_ref| / den, NaN-propagating: any non-finite GPU value where
+    the reference is finite counts as an infinite error."""
+    c = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c - c_ref) / den
+    bad = ~np.isfinite(c) & np.isfinite(c_ref)
+    if bad.any():
+        return float("inf")
+    if err.size == 0:
+        return 0.0
+    return float(np.max(err))

@@ -1,0 +1,198 @@
+/*
+ * CPU oracle for the general matrix multiply  C = alpha * A * B + beta * C.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * GPU library.
+ *
+ * What it computes (page "Naive GEMM and Roofline analysis", section 10.1,
+ * the GEMM definition): for every output row m and column n,
+ *
+ *     C_ref[m][n] = alpha * sum_{k=0}^{K-1} A[m][k] * B[k][n] + beta * C_in[m][n]
+ *
+ * with A, B and C stored densely row-major, A[m][k] at m*K+k, B[k][n] at
+ * k*N+n and C[m][n] at m*N+n, exactly the indexing of the naive kernel in
+ * section 10.2 of the same page.  The worked 2x2 example of page "From model
+ * computation to GPU execution", section 4.3, is the same dot-product view.
+ *
+ * Arithmetic is fp64 throughout: inputs are widened exactly (fp32 -> double,
+ * or a bf16 bit pattern -> fp32 -> double), the sum over k runs in ascending
+ * k order, and the result is kept in fp64, never rounded.  Beside each result
+ * the oracle returns the error denominator used by the parity tests,
+ *
+ *     den[m][n] = |alpha| * sum_k |A[m][k] * B[k][n]| + |beta * C_in[m][n]| + 1e-30,
+ *
+ * so that a GPU value c passes when |c - C_ref| / den is within tolerance.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - beta == 0: C_in is not read at all (it may be NULL or hold NaN); the
+ *     GEMM section of page "Where kernel performance comes from" assumes the
+ *     old C need not be read when beta is zero.
+ *   - K == 0: the sum is empty, so C_ref = beta * C_in (zeros when beta == 0).
+ *   - M == 0 or N == 0: nothing to do.
+ *
+ * The only parallelism is an OpenMP loop over independent output rows (or
+ * independent sampled entries); each row is the plain i-k-j triple loop.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+
+enum { ELEM_F32 = 0, ELEM_BF16 = 1 };
+
+/* Exact widening of one stored element to double. */
+static double load_elem(const void *base, int kind, int64_t idx)
+{
+    if (kind == ELEM_F32)
+        return (double)((const float *)base)[idx];
+    /* bf16 is the upper 16 bits of an IEEE binary32 value. */
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int check_args(int64_t M, int64_t N, int64_t K, double beta,
+                      const void *A, const void *B, const float *Cin,
+                      const double *Cref, const double *den)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_EINVAL;
+    if (M > 0 && K > 0 && A == NULL)
+        return ORACLE_EINVAL;
+    if (K > 0 && N > 0 && B == NULL)
+        return ORACLE_EINVAL;
+    if (M > 0 && N > 0 && (Cref == NULL || den == NULL))
+        return ORACLE_EINVAL;
+    if (M > 0 && N > 0 && beta != 0.0 && Cin == NULL)
+        return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* Full output: every (m, n), row by row, i-k-j order. */
+static int gemm_full(int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                     const void *A, const void *B, int kind, const float *Cin,
+                     double *Cref, double *den)
+{
+    int rc = check_args(M, N, K, beta, A, B, Cin, Cref, den);
+    if (rc != ORACLE_OK || M == 0 || N == 0)
+        return rc;
+
+    int64_t m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        double *acc = Cref + m * N; /* running sum over k   */
+        double *mag = den + m * N;  /* running sum of |A*B| */
+        for (int64_t n = 0; n < N; ++n) {
+            acc[n] = 0.0;
+            mag[n] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            double a = load_elem(A, kind, m * K + k);
+            for (int64_t n = 0; n < N; ++n) {
+                double p = a * load_elem(B, kind, k * N + n);
+                acc[n] += p;
+                mag[n] += fabs(p);
+            }
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double c_in = (beta != 0.0) ? (double)Cin[m * N + n] : 0.0;
+            acc[n] = alpha * acc[n] + beta * c_in;
+            mag[n] = fabs(alpha) * mag[n] + fabs(beta * c_in) + 1e-30;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Selected outputs only: entry e is (rows[e], cols[e]); one dot product each. */
+static int gemm_entries(int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                        const void *A, const void *B, int kind, const float *Cin,
+                        int64_t count, const int64_t *rows, const int64_t *cols,
+                        double *out, double *den)
+{
+    if (count < 0 || (count > 0 && (rows == NULL || cols == NULL || out == NULL || den == NULL)))
+        return ORACLE_EINVAL;
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_EINVAL;
+    if (count == 0)
+        return ORACLE_OK;
+    if (M == 0 || N == 0)
+        return ORACLE_EINVAL; /* there is no entry to sample */
+    if ((K > 0 && (A == NULL || B == NULL)) || (beta != 0.0 && Cin == NULL))
+        return ORACLE_EINVAL;
+    for (int64_t e = 0; e < count; ++e)
+        if (rows[e] < 0 || rows[e] >= M || cols[e] < 0 || cols[e] >= N)
+            return ORACLE_EINVAL;
+
+    int64_t e;
+#pragma omp parallel for schedule(static)
+    for (e = 0; e < count; ++e) {
+        int64_t m = rows[e], n = cols[e];
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = load_elem(A, kind, m * K + k) * load_elem(B, kind, k * N + n);
+            acc += p;
+            mag += fabs(p);
+        }
+        double c_in = (beta != 0.0) ? (double)Cin[m * N + n] : 0.0;
+        out[e] = alpha * acc + beta * c_in;
+        den[e] = fabs(alpha) * mag + fabs(beta * c_in) + 1e-30;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- exported entry points (plain C ABI, host pointers only) ---- */
+
+int oracle_gemm_f32(int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                    const float *A, const float *B, const float *Cin,
+                    double *Cref, double *den)
+{
+    return gemm_full(M, N, K, alpha, beta, A, B, ELEM_F32, Cin, Cref, den);
+}
+
+int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                     const uint16_t *A, const uint16_t *B, const float *Cin,
+                     double *Cref, double *den)
+{
+    return gemm_full(M, N, K, alpha, beta, A, B, ELEM_BF16, Cin, Cref, den);
+}
+
+int oracle_gemm_f32_entries(int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                            const float *A, const float *B, const float *Cin,
+                            int64_t count, const int64_t *rows, const int64_t *cols,
+                            double *out, double *den)
+{
+    return gemm_entries(M, N, K, alpha, beta, A, B, ELEM_F32, Cin, count, rows, cols, out, den);
+}
+
+int oracle_gemm_bf16_entries(int64_t M, int64_t N, int64_t K, double alpha, double beta,
+                             const uint16_t *A, const uint16_t *B, const float *Cin,
+                             int64_t count, const int64_t *rows, const int64_t *cols,
+                             double *out, double *den)
+{
+    return gemm_entries(M, N, K, alpha, beta, A, B, ELEM_BF16, Cin, count, rows, cols, out, den);
+}
+
+/* Number of OpenMP threads a parallel region of this library would use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+#else
+    return 1;
+#endif
+}

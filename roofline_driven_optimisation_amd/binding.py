@@ -1,0 +1,150 @@
+"""Thin ctypes binding over libgemm.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+checks tensor dtypes, shapes, devices and contiguity, then passes raw device
+pointers and the HIP stream handle to the C entry points declared in
+``include/gemm.h``.  There is no fallback: if the library is missing, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgemm.so"
+
+GEMM_OK = 0
+_lock = threading.Lock()
+_lib = None
+
+
+class GemmError(RuntimeError):
+    """A non-zero status returned by the C library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("gemm failed with status %d: %s" % (status, message))
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def library():
+    """Load libgemm.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "%s is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')"
+                % path)
+        lib = ctypes.CDLL(path)
+        i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        for name in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [i, i, i, f, f, vp, vp, vp, vp]
+            fn.restype = ctypes.c_int
+        lib.gemm_status_string.argtypes = [ctypes.c_int]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_last_kernel.argtypes = []
+        lib.gemm_last_kernel.restype = ctypes.c_char_p
+        lib.gemm_abi_version.argtypes = []
+        lib.gemm_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _status_message(status: int) -> str:
+    return library().gemm_status_string(status).decode()
+
+
+def last_kernel() -> str:
+    """Name of the kernel the last call on this thread launched."""
+    return library().gemm_last_kernel().decode()
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(A, B, C, in_dtype):
+    import torch
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU" % name)
+        if t.dim() != 2:
+            raise ValueError("%s must be 2-D" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous (packed row-major)" % name)
+    if A.dtype != in_dtype or B.dtype != in_dtype:
+        raise TypeError("A and B must be %s" % in_dtype)
+    if C.dtype != torch.float32:
+        raise TypeError("C must be float32")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on one device")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    return int(M), int(N), int(K)
+
+
+def _call(fn_name, A, B, C, alpha, beta, stream, in_dtype):
+    import torch
+    M, N, K = _check(A, B, C, in_dtype)
+    lib = library()
+    with torch.cuda.device(C.device):
+        status = getattr(lib, fn_name)(M, N, K, float(alpha), float(beta),
+                                       ctypes.c_void_p(A.data_ptr()),
+                                       ctypes.c_void_p(B.data_ptr()),
+                                       ctypes.c_void_p(C.data_ptr()),
+                                       _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
+    return C
+
+
+def gemm_f32(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """C = alpha*A@B + beta*C with float32 A (M x K), B (K x N), C (M x N)."""
+    import torch
+    return _call("gemm_f32", A, B, C, alpha, beta, stream, torch.float32)
+
+
+def gemm_bf16(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """C = alpha*A@B + beta*C with bfloat16 A and B, float32 C."""
+    import torch
+    return _call("gemm_bf16", A, B, C, alpha, beta, stream, torch.bfloat16)
+
+
+def gemm_naive_f32(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """The one-thread-per-output kernel (the unoptimised starting point)."""
+    import torch
+    return _call("gemm_naive_f32", A, B, C, alpha, beta, stream, torch.float32)
+
+
+def gemm_naive_bf16(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    import torch
+    return _call("gemm_naive_bf16", A, B, C, alpha, beta, stream, torch.bfloat16)
+
+
+def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """Dispatch on A's dtype: float32 -> gemm_f32, bfloat16 -> gemm_bf16."""
+    import torch
+    if A.dtype == torch.float32:
+        return gemm_f32(A, B, C, alpha, beta, stream)
+    if A.dtype == torch.bfloat16:
+        return gemm_bf16(A, B, C, alpha, beta, stream)
+    raise TypeError("unsupported dtype %s" % A.dtype)
