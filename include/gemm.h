@@ -1,0 +1,114 @@
+/*
+ * gemm.h -- C ABI of libgemm.so, a GEMM library for AMD MI355X (gfx950).
+ *
+ * Operation (page "Naive GEMM and Roofline analysis", section 10.1, the GEMM
+ * definition):
+ *
+ *     C[m][n] = alpha * sum_k A[m][k] * B[k][n] + beta * C[m][n]
+ *
+ * Layout.  Every matrix is dense and row-major with no padding, as in the
+ * naive kernel of section 10.2 of that page: A is M x K (A[m][k] at m*K+k),
+ * B is K x N (B[k][n] at k*N+n), C is M x N (C[m][n] at m*N+n).  There are no
+ * transpose flags and no leading-dimension arguments.
+ *
+ * Pointers.  A, B and C are DEVICE pointers on the current HIP device.
+ * ``stream`` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ * is enqueued on that stream and the call returns without waiting for it;
+ * a fault inside a kernel surfaces at the caller's next synchronisation.
+ *
+ * Ownership.  The caller owns A, B, C and the stream.  A and B are only read.
+ * C is read (only when beta != 0) and written in place.  C must not overlap A
+ * or B.  The library keeps no pointer after the call returns.
+ *
+ * Special cases.  M == 0 or N == 0: returns GEMM_OK and launches nothing.
+ * K == 0: C = beta * C (zeros when beta == 0).  beta == 0: C is never read, so
+ * it may hold NaN or garbage.  Any shape and any pointer alignment is
+ * accepted; fast vectorised kernels run when rows are 16-byte aligned, other
+ * inputs go to slower kernels that load element by element.
+ *
+ * Workspace.  The decode-shaped (skinny-M) bf16 path splits K across
+ * workgroups and needs a scratch area for partial sums.  The library
+ * allocates it lazily (hipMalloc) on the first such call for a given
+ * (device, stream) pair and reuses it afterwards; it is never freed before
+ * process exit.  Concurrent calls on different streams get different
+ * workspaces; concurrent calls from several host threads on one stream must
+ * be serialised by the caller, as the stream would serialise them anyway.
+ *
+ * Errors.  No call aborts or throws across the ABI.  Negative sizes, or a
+ * NULL pointer for a matrix with a non-zero number of elements, return
+ * GEMM_ERR_INVALID_ARG and launch nothing.  A failed
+ * launch returns GEMM_ERR_LAUNCH, a failed workspace allocation
+ * GEMM_ERR_ALLOC and a failed device query GEMM_ERR_DEVICE.
+ */
+#ifndef MI355X_GEMM_H
+#define MI355X_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GEMM_API __attribute__((visibility("default")))
+#else
+#define GEMM_API
+#endif
+
+enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,
+    GEMM_ERR_LAUNCH = 2,
+    GEMM_ERR_ALLOC = 3,
+    GEMM_ERR_DEVICE = 4
+};
+
+/*
+ * fp32 GEMM: A, B and C are float32.  Products and sums are fp32 (matrix-core
+ * fp32 MFMA on the tiled path); alpha and beta are applied in fp32 in the
+ * kernel's epilogue.
+ */
+GEMM_API int gemm_f32(int M, int N, int K, float alpha, float beta,
+             const float *A, const float *B, float *C, void *stream);
+
+/*
+ * bf16-input GEMM: A and B hold bf16 bit patterns (the upper 16 bits of an
+ * IEEE binary32); C is float32 in and out.  Products are exact in fp32 and
+ * are accumulated in fp32.  M <= 16 runs the HBM-streaming decode kernel,
+ * larger M the LDS-tiled MFMA kernel.
+ */
+GEMM_API int gemm_bf16(int M, int N, int K, float alpha, float beta,
+              const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/*
+ * The unoptimised starting point of section 10.2 of page "Naive GEMM and
+ * Roofline analysis": one thread per output element, a plain loop over k,
+ * 16 x 16 thread blocks, with the full alpha/beta update.  Same arguments and
+ * semantics as gemm_f32 / gemm_bf16; kept as the first rung of the
+ * optimisation ladder and as a correctness cross-check.
+ */
+GEMM_API int gemm_naive_f32(int M, int N, int K, float alpha, float beta,
+                   const float *A, const float *B, float *C, void *stream);
+GEMM_API int gemm_naive_bf16(int M, int N, int K, float alpha, float beta,
+                    const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/* Static English text for a gemm_status value (never NULL). */
+GEMM_API const char *gemm_status_string(int status);
+
+/*
+ * Name of the kernel the most recent gemm_* call made on the calling host
+ * thread launched ("none" if it launched nothing).  Static storage; valid
+ * until the next call on the same thread.  For tests and benchmarks.
+ */
+GEMM_API const char *gemm_last_kernel(void);
+
+/* GEMM_ABI_VERSION of the built library. */
+GEMM_API int gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355X_GEMM_H */

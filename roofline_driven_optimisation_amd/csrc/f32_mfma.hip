@@ -1,0 +1,188 @@
+// fp32 GEMM on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), LDS-tiled.
+//
+// Structure (page "Naive GEMM and Roofline analysis", section 10.4: block
+// tile -> warp tile -> matrix instruction, with double buffering):
+//   * workgroup tile 128 x 128, K step 32, 256 threads = 4 waves of 64 lanes
+//     in a 2 x 2 arrangement, each wave owning a 64 x 64 sub-tile made of
+//     2 x 2 MFMA blocks of 32 x 32;
+//   * A and B tiles are staged through two LDS buffers; the next tile's
+//     global loads are issued into registers before the current tile's MFMAs
+//     and written to the other buffer afterwards, so one barrier per K step
+//     suffices (page "Where kernel performance comes from", overlap section:
+//     load k+1 while computing k);
+//   * the fused epilogue applies alpha and beta in fp32 and never reads C when
+//     beta == 0.
+//
+// gfx950 has no reduced-precision fp32 matrix path to fall into: products and
+// sums stay fp32.  The fp32 MFMA and the VALU have the same published peak,
+// and without packed fp32 math the VALU reaches only half of it, so the matrix
+// core is the only way to the fp32 roofline here.
+//
+// LDS layout: A is stored transposed, As[k][m], so that the MFMA A operand
+// (lane l reads row l % 32 at k = l / 32) is a conflict-free 32-float row
+// read; B stays Bs[k][n] as it comes from global memory.  Rows are padded by 4
+// floats.  Out-of-range rows and columns are zero-filled on load and never
+// stored (the edge handling of section 10.6 of the same page).
+#include "common.h"
+#include "kernels.h"
+
+namespace mgemm {
+
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kPad = 4;
+constexpr int kLdA = kBM + kPad;  // floats per As row (one k)
+constexpr int kLdB = kBN + kPad;  // floats per Bs row (one k)
+constexpr int kThreads = 256;
+constexpr int kAChunks = kBM * kBK / 4 / kThreads;  // float4 chunks of A per thread (4)
+constexpr int kBChunks = kBK * kBN / 4 / kThreads;  // float4 chunks of B per thread (4)
+
+template <bool VEC>
+__device__ __forceinline__ f32x4 load4(const float *__restrict__ base, size_t row_off, int col,
+                                       int ncols, bool row_ok) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (VEC) {
+        // ncols % 4 == 0 and col % 4 == 0: the chunk is wholly in or out
+        if (row_ok && col < ncols) v = *reinterpret_cast<const f32x4 *>(base + row_off + col);
+    } else if (row_ok) {
+        if (col + 0 < ncols) v.x = base[row_off + col + 0];
+        if (col + 1 < ncols) v.y = base[row_off + col + 1];
+        if (col + 2 < ncols) v.z = base[row_off + col + 2];
+        if (col + 3 < ncols) v.w = base[row_off + col + 3];
+    }
+    return v;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int K, float alpha,
+                                                               float beta,
+                                                               const float *__restrict__ A,
+                                                               const float *__restrict__ B,
+                                                               float *C, int tiles_m,
+                                                               int tiles_n) {
+    __shared__ float As[2][kBK][kLdA];
+    __shared__ float Bs[2][kBK][kLdB];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tm, tn);
+    const int m0 = tm * kBM, n0 = tn * kBN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // Global -> register staging.  A chunk c: row c / 8, k-quad c % 8 (eight
+    // lanes cover one 128-byte row segment).  B chunk c: k-row c / 32,
+    // n-quad c % 32 (a wave covers two 512-byte row segments).
+    f32x4 ra[kAChunks], rb[kBChunks];
+
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < kAChunks; ++i) {
+            const int c = tid + kThreads * i;
+            const int row = m0 + (c >> 3);
+            ra[i] = load4<VEC>(A, static_cast<size_t>(row) * K, k0 + (c & 7) * 4, K, row < M);
+        }
+#pragma unroll
+        for (int i = 0; i < kBChunks; ++i) {
+            const int c = tid + kThreads * i;
+            const int kr = k0 + (c >> 5);
+            rb[i] = load4<VEC>(B, static_cast<size_t>(kr) * N, n0 + (c & 31) * 4, N, kr < K);
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kAChunks; ++i) {
+            const int c = tid + kThreads * i;
+            const int r = c >> 3, kq = (c & 7) * 4;
+            As[buf][kq + 0][r] = ra[i].x;
+            As[buf][kq + 1][r] = ra[i].y;
+            As[buf][kq + 2][r] = ra[i].z;
+            As[buf][kq + 3][r] = ra[i].w;
+        }
+#pragma unroll
+        for (int i = 0; i < kBChunks; ++i) {
+            const int c = tid + kThreads * i;
+            *reinterpret_cast<f32x4 *>(&Bs[buf][c >> 5][(c & 31) * 4]) = rb[i];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int ktiles = (K + kBK - 1) / kBK;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ktiles; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < ktiles) load_tile((t + 1) * kBK);
+#pragma unroll
+        for (int s = 0; s < kBK / 2; ++s) {
+            const int kk = 2 * s + h;
+            const float a0 = As[cur][kk][wm * 64 + l32];
+            const float a1 = As[cur][kk][wm * 64 + 32 + l32];
+            const float b0 = Bs[cur][kk][wn * 64 + l32];
+            const float b1 = Bs[cur][kk][wn * 64 + 32 + l32];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        if (t + 1 < ktiles) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.  Accumulator register r of a 32 x 32 block holds row
+    // 8 * (r / 4) + 4 * (lane / 32) + r % 4 and column lane % 32.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + 32 * j + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < M && col < N) {
+                    const size_t idx = static_cast<size_t>(row) * N + col;
+                    float out = alpha * acc[i][j][r];
+                    if (beta != 0.0f) out = fmaf(beta, C[idx], out);
+                    C[idx] = out;
+                }
+            }
+        }
+}
+
+}  // namespace
+
+const char *f32_mfma_name(bool vec) {
+    return vec ? "f32_mfma_128x128x32_vec4" : "f32_mfma_128x128x32_scalar";
+}
+
+hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const float *A,
+                           const float *B, float *C, bool vec, hipStream_t stream) {
+    const long long tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    if (vec)
+        f32_mfma_kernel<true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                          static_cast<int>(tiles_m),
+                                                          static_cast<int>(tiles_n));
+    else
+        f32_mfma_kernel<false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                           static_cast<int>(tiles_m),
+                                                           static_cast<int>(tiles_n));
+    return hipGetLastError();
+}
+
+}  // namespace mgemm

@@ -1,0 +1,90 @@
+// The unoptimised starting point: one thread per output element.
+//
+// Page "Naive GEMM and Roofline analysis", section 10.2: each thread walks k
+// and accumulates A[row][k] * B[k][col]; threadIdx.x runs along columns so a
+// wavefront's B reads are contiguous (section 10.3.2 explains why the other
+// mapping is several times slower); blocks are 16 x 16 threads.  Unlike the
+// page's listing this one applies the full alpha/beta update, accepts bf16
+// inputs, and flattens the grid to one dimension.  Its per-thread arithmetic
+// intensity is 2K / (8K + 4), about 1/4 FLOP per byte, so it is left far
+// below the roofline on purpose.
+#include "common.h"
+#include "kernels.h"
+
+namespace mgemm {
+
+namespace {
+
+__device__ __forceinline__ float load_elem(const float *p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t *p, size_t i) {
+    return bf16_bits_to_float(p[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float alpha, float beta,
+                                                    const T *__restrict__ A,
+                                                    const T *__restrict__ B, float *C,
+                                                    int tiles_n) {
+    const int tile = blockIdx.x;
+    const int row = (tile / tiles_n) * 16 + threadIdx.y;
+    const int col = (tile % tiles_n) * 16 + threadIdx.x;
+    if (row >= M || col >= N) return;
+    const T *a = A + static_cast<size_t>(row) * K;
+    const T *b = B + col;
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum = fmaf(load_elem(a, k), load_elem(b, static_cast<size_t>(k) * N), sum);
+    const size_t idx = static_cast<size_t>(row) * N + col;
+    float out = alpha * sum;
+    if (beta != 0.0f) out = fmaf(beta, C[idx], out);
+    C[idx] = out;
+}
+
+__global__ __launch_bounds__(256) void scale_kernel(size_t count, float beta, float *C) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride)
+        C[i] = (beta != 0.0f) ? beta * C[i] : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void zero_ints_kernel(int *p, int count) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
+template <typename T>
+hipError_t launch_naive(int M, int N, int K, float alpha, float beta, const T *A, const T *B,
+                        float *C, hipStream_t stream) {
+    const long long tiles_m = (M + 15) / 16, tiles_n = (N + 15) / 16;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    naive_kernel<T><<<dim3(static_cast<unsigned>(tiles)), dim3(16, 16), 0, stream>>>(
+        M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_n));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_naive_f32(int M, int N, int K, float alpha, float beta, const float *A,
+                            const float *B, float *C, hipStream_t stream) {
+    return launch_naive<float>(M, N, K, alpha, beta, A, B, C, stream);
+}
+
+hipError_t launch_naive_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
+                             const uint16_t *B, float *C, hipStream_t stream) {
+    return launch_naive<uint16_t>(M, N, K, alpha, beta, A, B, C, stream);
+}
+
+hipError_t launch_scale_c(int M, int N, float beta, float *C, hipStream_t stream) {
+    const size_t count = static_cast<size_t>(M) * N;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    scale_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(count, beta, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_ints(int *p, int count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    zero_ints_kernel<<<dim3((count + 255) / 256), dim3(256), 0, stream>>>(p, count);
+    return hipGetLastError();
+}
+
+}  // namespace mgemm
