@@ -1,0 +1,247 @@
+"""Benchmark of the GEMM library on one MI355X; prints ONE JSON line.
+
+A step is one call of the hot path on the headline workload, bf16-input /
+fp32-accumulate GEMM at M = N = K = 4096 (alpha = 1, beta = 0), with inputs
+already resident in HBM.  ``value`` is that GEMM's throughput in TFLOP/s over
+exactly ``--steps`` timed steps (after ``--warmup`` untimed ones), bracketed
+by device synchronisations.  The same line carries:
+
+* ``roofline``: the dominant kernel's achieved TFLOP/s (2*M*N*K per launch
+  over the average launch time from HIP events recorded on the launch
+  stream) against the bf16 MFMA peak, plus HBM traffic from rocprofv3
+  counters when a counter summary for the current kernel source exists;
+* ``also``: the other workloads (fp32 4096^3 and 4092^3 with alpha 1.5 and
+  beta 0.5, LLaMA-7B prefill projections, decode-shaped GEMMs) with TFLOP/s,
+  algorithmic GB/s and their own roofline fraction;
+* ``cpu_baseline``: the CPU oracle, as it stands, timed on a bounded sample
+  of the headline workload (rank 0, N = 1 only).
+
+Every timed launch cycles through several copies of the operands whose total
+exceeds twice the 256 MB last-level cache, so each launch streams from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from roofline_driven_optimisation_amd import roofline as rl  # noqa: E402
+from roofline_driven_optimisation_amd.inputs import workload  # noqa: E402
+
+HEADLINE = "bf16_4096"
+SECONDARY = ["f32_4096", "f32_4092", "prefill_qkv", "prefill_o", "prefill_gate_up",
+             "prefill_down", "decode_up_m1", "decode_up_m8", "decode_up_m16",
+             "decode_down_m1", "decode_down_m8", "decode_down_m16", "decode_lm_head"]
+ROTATE_BYTES = 2 * 256 * 2 ** 20  # twice the MI355X Infinity Cache
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kernel_name: str) -> str:
+    """Hash of the source file that defines a kernel family (to tell whether
+    stored counter readings still describe the current code)."""
+    fam = {"bf16_mfma": "bf16_mfma.hip", "f32_mfma": "f32_mfma.hip",
+           "skinny": "skinny_bf16.hip", "naive": "naive.hip"}
+    for prefix, fname in fam.items():
+        if kernel_name.startswith(prefix):
+            path = os.path.join(ROOT, "roofline_driven_optimisation_amd", "csrc", fname)
+            return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return ""
+
+
+def stored_traffic(kernel_name: str, workload_name: str):
+    """HBM bytes per launch from a committed counter summary, or None.
+
+    The summary (profiles/counters_<kernel>_<workload>.md) states the source
+    hash it was taken with and the calibrated FETCH/WRITE bytes per dispatch;
+    a different hash means the kernel changed and the reading is stale.
+    """
+    path = os.path.join(ROOT, "profiles", "counters_%s_%s.md" % (kernel_name, workload_name))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(kernel_name):
+        return None
+    return float(m_bytes.group(1))
+
+
+class Prepared:
+    """Device copies of one workload's operands, rotated across launches."""
+
+    def __init__(self, name: str, seed: int = 0):
+        import torch
+        self.w = workload(name)
+        case = self.w.case(seed)
+        self.case = case
+        if case.bf16:
+            A = torch.from_numpy(case.A.view(np.int16)).view(torch.bfloat16)
+            B = torch.from_numpy(case.B.view(np.int16)).view(torch.bfloat16)
+        else:
+            A = torch.from_numpy(case.A)
+            B = torch.from_numpy(case.B)
+        C = (torch.from_numpy(case.C) if case.C is not None
+             else torch.zeros(case.M, case.N, dtype=torch.float32))
+        per_set = (A.numel() * A.element_size() + B.numel() * B.element_size()
+                   + C.numel() * C.element_size())
+        self.sets = max(1, -(-ROTATE_BYTES // per_set))
+        A, B, C = A.cuda(), B.cuda(), C.cuda()
+        self.bufs = [(A, B, C)] + [(A.clone(), B.clone(), C.clone()) for _ in range(self.sets - 1)]
+        self.C0 = C.clone() if case.C is not None else None
+        self.rf = rl.gemm_roofline(case.M, case.N, case.K, case.dtype, case.beta != 0.0)
+
+    def launch(self, i: int):
+        from roofline_driven_optimisation_amd import binding
+        A, B, C = self.bufs[i % self.sets]
+        binding.gemm(A, B, C, self.w.alpha, self.w.beta)
+
+    def kernel_name(self) -> str:
+        from roofline_driven_optimisation_amd import binding
+        self.launch(0)
+        return binding.last_kernel()
+
+
+def time_workload(p: Prepared, steps: int, warmup: int):
+    """(wall seconds per step, event seconds per launch) over `steps` launches."""
+    import torch
+    for i in range(warmup):
+        p.launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        p.launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    event = start.elapsed_time(end) * 1e-3 / steps
+    return wall, event
+
+
+def summary(p: Prepared, sec: float, kname: str) -> dict:
+    tflops = p.rf.flops / sec / 1e12
+    gbs = p.rf.nbytes / sec / 1e9
+    return {
+        "workload": p.w.name, "M": p.w.M, "N": p.w.N, "K": p.w.K, "dtype": p.w.dtype,
+        "alpha": p.w.alpha, "beta": p.w.beta, "kernel": kname, "us": round(sec * 1e6, 2),
+        "tflops": round(tflops, 2), "gbs": round(gbs, 1), "bound": p.rf.bound,
+        "roofline_tflops": round(p.rf.attainable / 1e12, 1),
+        "frac": round(p.rf.fraction(sec), 4),
+    }
+
+
+def cpu_baseline(budget_s: float = 12.0) -> dict:
+    """The CPU oracle, as it stands, timed on the leading rows of the headline
+    workload: a short calibration run sizes one sample of about budget_s."""
+    import oracle
+    oracle.build(force=False)
+    w = workload(HEADLINE)
+    case = w.case()
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    oracle.gemm(case.A[:32], case.B, None, w.alpha, 0.0, bf16=True)
+    rate = 2.0 * 32 * w.N * w.K / (time.perf_counter() - t0)
+    rows = int(max(32, min(w.M, budget_s * rate / (2.0 * w.N * w.K))))
+    t0 = time.perf_counter()
+    oracle.gemm(case.A[:rows], case.B, None, w.alpha, 0.0, bf16=True)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "rows 0..%d of the bf16 4096^3 GEMM (%dx4096 outputs, K=4096), "
+                      "fp64 i-k-j loop, %.1f s" % (rows - 1, rows, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--secondary-steps", type=int, default=50)
+    ap.add_argument("--only", default="", help="comma-separated workloads to time "
+                    "(profiling runs); skips the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has "
+              "no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.only:
+        for name in args.only.split(","):
+            p = Prepared(name)
+            kname = p.kernel_name()
+            wall, ev = time_workload(p, args.steps, args.warmup)
+            log(json.dumps(summary(p, ev, kname)))
+        return
+
+    log("bench: preparing %s" % HEADLINE)
+    head = Prepared(HEADLINE)
+    kname = head.kernel_name()
+    log("bench: timing %s (%s), %d steps" % (HEADLINE, kname, args.steps))
+    wall, ev = time_workload(head, args.steps, args.warmup)
+
+    also = []
+    for name in SECONDARY:
+        log("bench: secondary %s" % name)
+        p = Prepared(name)
+        kn = p.kernel_name()
+        _, sec = time_workload(p, args.secondary_steps, max(3, args.warmup // 4))
+        s = summary(p, sec, kn)
+        log("  " + json.dumps(s))
+        also.append(s)
+        del p
+        torch.cuda.empty_cache()
+
+    traffic = stored_traffic(kname, HEADLINE)
+    achieved = head.rf.flops / ev / 1e12
+    peak = rl.MI355X_PEAK_BF16 / 1e12
+    result = {
+        "metric": "GEMM TFLOP/s and % of roofline at M=N=K=4096 (fp32, bf16) + skinny-M GB/s",
+        "value": round(head.rf.flops / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: A, B ~ normal(0, 1/64) rounded to bf16, seed 0",
+        "config": {"workload": "bf16-input fp32-accumulate GEMM M=N=K=4096, alpha=1, beta=0, "
+                               "row-major, C fp32", "kernel": kname,
+                   "rotated_operand_sets": head.sets},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic},
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,6 +7,7 @@ go to ``_build/`` beside the sources.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import glob
 import os
 import subprocess
@@ -53,6 +54,12 @@ def build(verbose: bool = False, extra=()) -> str:
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (proc.stdout, proc.stderr))
+    # a kernel whose host stub was not emitted only shows up at load time
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as exc:
+        os.unlink(tmp)
+        raise RuntimeError("built library does not load: %s" % exc)
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -26,8 +26,8 @@ hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const f
                            const float *B, float *C, bool vec, hipStream_t stream);
 const char *f32_mfma_name(bool vec);
 
-// bf16 LDS-tiled MFMA kernel.  Needs K % 8 == 0, N % 8 == 0 and 16-byte
-// aligned A and B.  `cfg` indexes bf16_tile_configs().
+// bf16 LDS-tiled MFMA kernel.  Needs K % 8 == 0, N % 8 == 0, 16-byte
+// aligned A and B, K <= 2^21 and N <= 2^20.  `cfg` indexes the tile table.
 struct Bf16TileConfig {
     int bm, bn;
     const char *name;
@@ -42,7 +42,8 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
 // K % 8 == 0, N % 8 == 0 and 16-byte aligned A, B and C.  With splits > 1 the
 // K range is divided over `splits` workgroups per column block, which reduce
 // through `partials` (splits * M * N floats) and `counters` (one int per
-// column block, zero on entry and left zero on exit).
+// column block, zero on entry and left zero on exit); both must live in
+// uncached device memory (hipDeviceMallocUncached).
 constexpr int kSkinnyMaxM = 16;
 constexpr int kSkinnyCols = 128;  // output columns per workgroup
 int skinny_pick_splits(int M, int N, int K, int num_cus);

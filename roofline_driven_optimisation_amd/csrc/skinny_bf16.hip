@@ -27,6 +27,17 @@
 // block to finish (found with an atomic counter; the pages do not cover this
 // step) adds the partials in split order 0, 1, 2, ..., so results do not
 // depend on timing, applies alpha/beta, writes C and re-arms the counter.
+//
+// Cross-XCD visibility.  The eight XCDs of an MI355X have private L2 caches.
+// A device-scope fence makes a workgroup's stores visible to the others by
+// writing back and invalidating its whole L2, which measured 3-10x slower
+// than the streaming itself when every split workgroup does it.  The
+// workspace (partials and counters) is therefore allocated uncached
+// (hipDeviceMallocUncached): its loads and stores bypass the L2s and reach
+// memory directly.  A writer waits until its partial stores are acknowledged
+// (s_waitcnt 0) before the barrier and the counter increment, and the last
+// workgroup reads the partials only after its atomic has returned, so it
+// observes every partial without any L2 maintenance.
 #include "common.h"
 #include "kernels.h"
 
@@ -155,12 +166,11 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
         p[0] = f32x4{v[0], v[1], v[2], v[3]};
         p[1] = f32x4{v[4], v[5], v[6], v[7]};
     }
-    __threadfence();  // release the partials device-wide (all XCD L2s)
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
     __syncthreads();
     if (tid == 0) s_last = (atomicAdd(&counters[cb], 1) == splits - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();  // acquire the other workgroups' partials
 
     if (ok) {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -193,7 +203,7 @@ int skinny_pick_splits(int M, int N, int K, int num_cus) {
     (void)M;
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
-    const int target = 2 * num_cus;  // two workgroups per CU
+    const int target = num_cus + num_cus / 4;  // about 1.25 workgroups per CU (measured best)
     int splits = (target + col_blocks - 1) / col_blocks;
     const int max_splits = kblks / 8 > 1 ? kblks / 8 : 1;  // >= 8 k-blocks per workgroup
     if (splits > max_splits) splits = max_splits;
