@@ -22,7 +22,6 @@ exceeds twice the 256 MB last-level cache, so each launch streams from HBM.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -52,13 +51,8 @@ def log(msg):
 def kernel_source_hash(kernel_name: str) -> str:
     """Hash of the source file that defines a kernel family (to tell whether
     stored counter readings still describe the current code)."""
-    fam = {"bf16_mfma": "bf16_mfma.hip", "f32_mfma": "f32_mfma.hip",
-           "skinny": "skinny_bf16.hip", "naive": "naive.hip"}
-    for prefix, fname in fam.items():
-        if kernel_name.startswith(prefix):
-            path = os.path.join(ROOT, "roofline_driven_optimisation_amd", "csrc", fname)
-            return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
-    return ""
+    from roofline_driven_optimisation_amd.profiling import source_hash
+    return source_hash(kernel_name)
 
 
 def stored_traffic(kernel_name: str, workload_name: str):
@@ -176,6 +170,9 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated workloads to time "
                     "(profiling runs); skips the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, --steps times "
+                    "(calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -186,6 +183,22 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.warmup)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / args.steps
+        log(json.dumps({"copy_mib": args.copy_probe, "us": round(sec * 1e6, 2),
+                        "gbs_read_plus_write": round(2 * n / sec / 1e9, 1)}))
+        return
 
     if args.only:
         for name in args.only.split(","):

@@ -1,0 +1,130 @@
+"""Summaries of rocprofv3 CSV output (kernel statistics and HBM counters).
+
+Used to turn a profiling run of ``bench.py`` into the short text summaries
+kept beside the benchmark.  Two inputs:
+
+* ``--kernel-trace --stats --output-format csv`` writes ``*_kernel_stats.csv``
+  (per-kernel call count and durations);
+* ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` with ``--output-format csv``
+  write ``*_counter_collection.csv`` (one row per dispatch, values in KiB).
+
+HBM bytes per launch = median counter value x the calibration factor, where
+the factor makes a plain device copy of known size read and write exactly
+its size (counters are taken below L2, so MALL hits count as fabric traffic).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+KERNEL_SOURCES = {
+    "bf16_mfma": "bf16_mfma.hip",
+    "f32_mfma": "f32_mfma.hip",
+    "skinny": "skinny_bf16.hip",
+    "naive": "naive.hip",
+}
+
+
+def source_hash(kernel_family: str) -> str:
+    """sha256[:16] of the source that defines a kernel family."""
+    for prefix, fname in KERNEL_SOURCES.items():
+        if kernel_family.startswith(prefix):
+            with open(os.path.join(HERE, "csrc", fname), "rb") as f:
+                return hashlib.sha256(f.read()).hexdigest()[:16]
+    return ""
+
+
+def short_name(name: str) -> str:
+    """'void mgemm::(anonymous namespace)::bf16_mfma_kernel<256, 256, false>(...)'
+    -> 'bf16_mfma_kernel<256, 256, false>'."""
+    base = name.split("(")[0] if "(anonymous namespace)" not in name else \
+        name.split("::")[-1].split("(")[0]
+    if "(anonymous namespace)" in name:
+        tail = name.split("(anonymous namespace)::", 1)[1]
+        depth, out = 0, []
+        for ch in tail:
+            if ch == "(" and depth == 0:
+                break
+            depth += ch == "<"
+            depth -= ch == ">"
+            out.append(ch)
+        base = "".join(out)
+    return base.replace("void ", "").strip()
+
+
+def kernel_stats(path: str):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append({"kernel": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3,
+                         "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+                         "pct": float(r["Percentage"])})
+    return rows
+
+
+def counter_medians(path: str):
+    """{(kernel, counter): median value (KiB per dispatch)}."""
+    acc = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc[(short_name(r["Kernel_Name"]), r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in acc.items()}
+
+
+def stats_markdown(rows) -> str:
+    out = ["| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %s | %d | %.1f | %.1f | %.1f | %.2f |" % (
+            r["kernel"], r["calls"], r["avg_us"], r["min_us"], r["max_us"], r["pct"]))
+    return "\n".join(out)
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise FileNotFoundError("no *%s under %s" % (suffix, d))
+    return hits[0]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats", help="markdown table from a --kernel-trace --stats run")
+    s.add_argument("dir")
+    c = sub.add_parser("counters", help="calibrated HBM bytes per dispatch")
+    c.add_argument("--fetch", required=True, help="dir of the FETCH_SIZE run")
+    c.add_argument("--write", required=True, help="dir of the WRITE_SIZE run")
+    c.add_argument("--copy-fetch", required=True, help="dir of the copy probe's FETCH_SIZE run")
+    c.add_argument("--copy-write", required=True, help="dir of the copy probe's WRITE_SIZE run")
+    c.add_argument("--copy-mib", type=float, required=True)
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        print(stats_markdown(kernel_stats(_find(args.dir, "_kernel_stats.csv"))))
+        return
+    fetch = counter_medians(_find(args.fetch, "_counter_collection.csv"))
+    write = counter_medians(_find(args.write, "_counter_collection.csv"))
+    cf = counter_medians(_find(args.copy_fetch, "_counter_collection.csv"))
+    cw = counter_medians(_find(args.copy_write, "_counter_collection.csv"))
+    kib = args.copy_mib * 1024
+    f_fac = kib / max(v for (k, n), v in cf.items() if n == "FETCH_SIZE")
+    w_fac = kib / max(v for (k, n), v in cw.items() if n == "WRITE_SIZE")
+    print("calibration: copy of %.0f MiB -> FETCH_SIZE factor %.3f, WRITE_SIZE factor %.3f"
+          % (args.copy_mib, f_fac, w_fac))
+    for (k, n), v in sorted(fetch.items()):
+        w = write.get((k, "WRITE_SIZE"), float("nan"))
+        fb, wb = v * 1024 * f_fac, w * 1024 * w_fac
+        print("%s: fetch %.1f MB, write %.1f MB, total %.1f MB per dispatch (source %s)"
+              % (k, fb / 1e6, wb / 1e6, (fb + wb) / 1e6, source_hash(k)))
+
+
+if __name__ == "__main__":
+    main()
