@@ -1,8 +1,14 @@
 // bf16-input, fp32-accumulate GEMM on the gfx950 matrix cores
-// (v_mfma_f32_32x32x16_bf16), LDS-tiled and double-buffered.
+// (v_mfma_f32_32x32x16_bf16), LDS-tiled and multi-buffered.  Two kernels:
+//   * bf16_mfma_kernel: four waves, one per SIMD, K step 64, two LDS stages;
+//     each wave interleaves its LDS reads with its own MFMAs;
+//   * bf16_pp_kernel (further down): eight waves, two per SIMD, K step 32,
+//     four LDS stages; the two waves of a SIMD take turns reading fragments
+//     and running MFMAs (ping-pong), so MFMAs do not wait on LDS reads.
+// The tile picker at the end chooses between them by shape.
 //
-// Structure (page "Naive GEMM and Roofline analysis", section 10.4, the three
-// tile levels plus double buffering):
+// Structure of the four-wave kernel (page "Naive GEMM and Roofline
+// analysis", section 10.4, the three tile levels plus double buffering):
 //   * workgroup tile BM x BN (256 or 128 each), K step 64, 256 threads = four
 //     64-lane waves in 2 x 2, each owning a (BM/2) x (BN/2) sub-tile built from
 //     32 x 32 MFMA blocks; a 128 x 128 wave tile keeps 256 fp32 accumulators
@@ -23,19 +29,27 @@
 // matrix (which would otherwise wrap into the next row) is redirected to an
 // out-of-range offset.  The main loop has no branches on the shape.
 //
-// Operand layouts in LDS (rows of 16-byte chunks, XOR-swizzled, the software
-// form of the swizzled layouts of page "Memory hierarchy and cost table",
-// section 4.3.4):
+// Operand layouts in LDS.  The gfx950 LDS serves 256 bytes per clock (64
+// four-byte banks): a 16-byte-per-lane read is served 16 lanes per clock and
+// an 8-byte-per-lane read 32 lanes per clock, and each such lane group must
+// touch 64 distinct banks to run at full rate.  Rows are stored as 16-byte
+// chunks, XOR-swizzled (the software form of the swizzled layouts of page
+// "Memory hierarchy and cost table", section 4.3.4):
 //   * A tile: BM rows of 64 k (128 bytes, 8 chunks); chunk c of row r sits at
-//     position c ^ (r % 8).  A fragment (row l % 32, k-octet l / 32) is one
-//     ds_read_b128, and any 8 consecutive lanes hit 8 different bank groups.
-//   * B tile: 64 k-rows of BN n (natural row-major); chunk c of row k sits at
-//     position c ^ swz_b(k).  The B fragment needs 8 k-consecutive values of
-//     one column per lane; ds_read_b64_tr_b16 provides exactly that transpose:
-//     within a 16-lane group, lane i receives element i % 4 of the 8 bytes
-//     read by lanes 4e + i / 4 (e = 0..3).  So if lane j reads the 4 columns
-//     n0 + 4 (j % 4) .. +3 of row k0 + j / 4, lane i gets rows k0 .. k0+3 of
-//     column n0 + i; two such reads give the 8 k values of a fragment.
+//     position c ^ ((r / 2) % 8).  A fragment (row l % 32, k-octet l / 32) is
+//     one ds_read_b128; 16 consecutive rows share one chunk index, fall into
+//     two 128-byte halves of a bank line by parity and into 8 positions by
+//     the key, so every 16-lane group covers the 64 banks once.
+//   * B tile: 64 k-rows of BN n (natural row-major, 256 or 512 bytes);
+//     chunk c of row k sits at position c ^ swz_b(k).  The B fragment needs 8
+//     k-consecutive values of one column per lane; ds_read_b64_tr_b16
+//     provides that transpose: within a 16-lane group, lane i receives
+//     element i % 4 of the 8 bytes read by lanes 4e + i / 4 (e = 0..3).  So
+//     if lane j reads the 4 columns n0 + 4 (j % 4) .. +3 of row k0 + j / 4,
+//     lane i gets rows k0 .. k0+3 of column n0 + i; two such reads give the 8
+//     k values of a fragment.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -65,11 +79,16 @@ struct Tile {
     static constexpr int B_STAGE = kBK * BN;
 };
 
-// Swizzle key of B row k: the four rows read by one 16-lane group of a
-// transposed read land in four different 32-byte bank groups.  It depends on
-// k % 4 only, so a lane's read address changes by plain immediate offsets
-// across rows and k16 sub-steps.
-__device__ __forceinline__ int swz_b(int k) { return (k & 3) << 1; }
+// Swizzle key of B row k (XOR on chunk-index bits 2..3, i.e. on 64-byte
+// segments).  A 32-lane half of a transposed read covers 4 consecutive rows x
+// one aligned 64-byte segment; the key sends the 4 rows to the 4 different
+// 64-byte quarters of a 256-byte bank line.  It depends on k % 4 only, so a
+// lane's read address changes by plain immediate offsets across rows and k16
+// sub-steps.
+__device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
+
+// Swizzle key of A row r (see the layout notes above).
+__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes) {
     if (bytes < 0) bytes = 0;
@@ -93,7 +112,9 @@ __device__ __forceinline__ i32x4 make_desc(const void *base, long long bytes) {
 }
 
 // One direct global -> LDS copy: 16 bytes per lane from byte offset `voff`
-// of the buffer `desc` into LDS at `lds_addr` + 16 * lane.  Written as inline
+// of the buffer `desc` into LDS at `lds_addr` + 16 * lane.  sc0 makes the
+// load bypass the vector L1 (the data is used once per workgroup and lands
+// in LDS; about 4% faster on the square GEMM than a cached load).  Written as inline
 // assembly on purpose: the compiler then does not model it as an LDS write
 // and does not stall the fragment reads of the other stage behind it (it
 // cannot prove the two stages apart); the K loop waits for these copies
@@ -106,7 +127,7 @@ __device__ __forceinline__ void lds_dma16(i32x4 desc, uint32_t lds_addr, uint32_
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen sc0 lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "s"(lds_addr), "v"(voff), "s"(desc)
@@ -140,9 +161,10 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
 
     // ---- per-lane global offsets of this wave's direct-to-LDS loads --------
     // A load L = wave + 4 i covers tile rows 8L .. 8L+7; lane p fills chunk
-    // position p % 8 of row 8L + p / 8 with logical chunk (p % 8) ^ (p / 8).
+    // position p % 8 of row 8L + p / 8 with logical chunk (p % 8) ^ swz_a(row).
+    // The key of that row is the same for every i (8L = 8 wave + 32 i).
     const int a_row_in = lane >> 3;
-    const int a_chunk = (lane & 7) ^ a_row_in;
+    const int a_chunk = (lane & 7) ^ swz_a(8 * wave + a_row_in);
     // B load L = wave + 4 i covers rows L * R .. L * R + R - 1 (R rows per KB).
     const int b_row_in = lane / T::B_CHUNKS;
     const int b_pos = lane % T::B_CHUNKS;
@@ -162,25 +184,40 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     const uint32_t b_off = static_cast<uint32_t>((b_row0 * N + 8 * b_c) * 2);
     const uint32_t b_step = static_cast<uint32_t>(4 * T::B_ROWS_PER_LOAD * N * 2);
 
-    auto issue_tile = [&](int k0, int stage) {
+    // Direct copies of one K tile: loads 0 .. A_LOADS-1 are A, the rest B.
+    struct TileCopy {
+        i32x4 ra, rb;
+        uint32_t la, lb;
+        bool a_ok;
+    };
+    auto tile_copy = [&](int k0, int stage) {
+        TileCopy c;
         // descriptors based at the tile origin
-        const i32x4 ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
-                                   (static_cast<long long>(M - m0) * K - k0) * 2);
-        const i32x4 rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
-                                   (static_cast<long long>(K - k0) * N - n0) * 2);
-        const bool a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
-        const uint32_t la = lds_address(&lds_a[stage][wave * 512]);
-        const uint32_t lb = lds_address(&lds_b[stage][wave * 512]);
+        c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                         (static_cast<long long>(M - m0) * K - k0) * 2);
+        c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                         (static_cast<long long>(K - k0) * N - n0) * 2);
+        c.a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
+        c.la = lds_address(&lds_a[stage][wave * 512]);
+        c.lb = lds_address(&lds_b[stage][wave * 512]);
+        return c;
+    };
+    auto issue_copy = [&](const TileCopy &c, int q) {
+        if (q < T::A_LOADS)
+            lds_dma16(c.ra, c.la + q * 4 * 1024, c.a_ok ? a_off + q * a_step : kOOB);
+        else
+            lds_dma16(c.rb, c.lb + (q - T::A_LOADS) * 4 * 1024,
+                      b_ok ? b_off + (q - T::A_LOADS) * b_step : kOOB);
+    };
+    auto issue_tile = [&](int k0, int stage) {
+        const TileCopy c = tile_copy(k0, stage);
 #pragma unroll
-        for (int i = 0; i < T::A_LOADS; ++i)
-            lds_dma16(ra, la + i * 4 * 1024, a_ok ? a_off + i * a_step : kOOB);
-#pragma unroll
-        for (int i = 0; i < T::B_LOADS; ++i)
-            lds_dma16(rb, lb + i * 4 * 1024, b_ok ? b_off + i * b_step : kOOB);
+        for (int q = 0; q < T::A_LOADS + T::B_LOADS; ++q) issue_copy(c, q);
     };
 
     // ---- fragment reads ----------------------------------------------------
-    // A: row wm*WM + 32 i + l32, chunk 2 s + h at position chunk ^ (lane % 8).
+    // A: row wm*WM + 32 i + l32, chunk 2 s + h at position chunk ^ swz_a(l32)
+    //    (WM and 32 i are multiples of 16, so the key depends on l32 only).
     // B: lane's transposed-read address: row 16 s + 8 h' + 4 r + j / 4 and
     //    columns n_frag + 4 (j % 4), where j = lane % 16, h' = (lane / 32).
     const int a_lane_base = (wm * T::WM + l32) * kBK;
@@ -188,33 +225,31 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     const int b_col_lane = wn * T::WN + 16 * (g & 1) + 4 * (j16 & 3);  // + 32 j
     const int b_row_lane = 8 * (g >> 1) + (j16 >> 2);                  // + 16 s + 4 r
 
-    auto read_frags = [&](int stage, int s, bf16x8 (&a)[T::MI], bf16x8 (&b)[T::NI]) {
-        const uint16_t *sa = lds_a[stage];
-        const uint16_t *sb = lds_b[stage];
-        const int pos = ((2 * s + h) ^ (lane & 7)) * 8;
-#pragma unroll
-        for (int i = 0; i < T::MI; ++i) {
+    // Fragment read number q of k16 sub-step s: q < MI reads A block q, the
+    // rest read half (q - MI) % 2 of B block (q - MI) / 2.
+    constexpr int kReads = T::MI + 2 * T::NI;
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    auto read_one = [&](int stage, int s, int q, bf16x8 (&a)[T::MI], s16x8 (&b)[T::NI]) {
+        if (q < T::MI) {
+            const int pos = ((2 * s + h) ^ swz_a(l32)) * 8;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(
-                &sa[a_lane_base + 32 * i * kBK + pos]);
-            a[i] = __builtin_bit_cast(bf16x8, v);
-        }
+                &lds_a[stage][a_lane_base + 32 * q * kBK + pos]);
+            a[q] = __builtin_bit_cast(bf16x8, v);
+        } else {
+            const int jj = (q - T::MI) >> 1, r = (q - T::MI) & 1;
+            const int row = 16 * s + 4 * r + b_row_lane;
+            const int col = b_col_lane + 32 * jj;
+            const int chunk = (col >> 3) ^ swz_b(row);
+            const int elem = row * BN + chunk * 8 + (col & 7);
+            const s16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)&lds_b[stage][elem]);
 #pragma unroll
-        for (int jj = 0; jj < T::NI; ++jj) {
-            s16x4 part[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int row = 16 * s + 4 * r + b_row_lane;
-                const int col = b_col_lane + 32 * jj;
-                const int chunk = (col >> 3) ^ swz_b(row);
-                const int elem = row * BN + chunk * 8 + (col & 7);
-                part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (s16x4 __attribute__((address_space(3))) *)&sb[elem]);
-            }
-            const s16x4 lo = part[0], hi = part[1];
-            typedef short s16x8 __attribute__((ext_vector_type(8)));
-            const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            b[jj] = __builtin_bit_cast(bf16x8, both);
+            for (int e = 0; e < 4; ++e) b[jj][4 * r + e] = part[e];
         }
+    };
+    auto read_frags = [&](int stage, int s, bf16x8 (&a)[T::MI], s16x8 (&b)[T::NI]) {
+#pragma unroll
+        for (int q = 0; q < kReads; ++q) read_one(stage, s, q, a, b);
     };
 
     f32x16 acc[T::MI][T::NI];
@@ -240,34 +275,59 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     // out of range and only write zeros into the idle stage.  Scheduling
     // barriers keep each sub-step's fragment reads (and the step's global
     // loads) interleaved with its MFMAs.
-    bf16x8 fa[2][T::MI], fb[2][T::NI];
+    bf16x8 fa[2][T::MI];
+    s16x8 fb[2][T::NI];
     read_frags(0, 0, fa[0], fb[0]);
+    constexpr int kMfma = T::MI * T::NI;
+    constexpr int kCopies = T::A_LOADS + T::B_LOADS;
     for (int t = 0; t < ktiles; ++t) {
         const int cur = t & 1;
-        issue_tile((t + 1) * kBK, cur ^ 1);
+        const TileCopy copy = tile_copy((t + 1) * kBK, cur ^ 1);
 #pragma unroll
         for (int s = 0; s < kBK / 16; ++s) {
             const int f = s & 1;
-            if (s + 1 < kBK / 16) {
-                read_frags(cur, s + 1, fa[f ^ 1], fb[f ^ 1]);
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);  // own loads of tile t+1 landed, reads done
-                __syncthreads();
-                read_frags(cur ^ 1, 0, fa[f ^ 1], fb[f ^ 1]);
+            const bool last = (s + 1 == kBK / 16);
+            // Manual schedule: MFMA q is followed by fragment read q of the
+            // next sub-step and, in sub-step 0, by global->LDS copy q.  In
+            // the last sub-step the first half of the MFMAs runs before the
+            // barrier and the next tile's reads follow it.
+            constexpr int kHalf = kMfma / 2;
+            constexpr int kReadsPerSlot = (kReads + kMfma - 1) / kMfma;
+            constexpr int kReadsPerLateSlot = (kReads + (kMfma - kHalf) - 1) / (kMfma - kHalf);
+            constexpr int kCopiesPerSlot = (kCopies + kMfma - 1) / kMfma;
+#pragma unroll
+            for (int q = 0; q < kMfma; ++q) {
+                const int i = q / T::NI, jj = q % T::NI;
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    fa[f][i], __builtin_bit_cast(bf16x8, fb[f][jj]), acc[i][jj], 0, 0, 0);
+                if (!last) {
+#pragma unroll
+                    for (int u = 0; u < kReadsPerSlot; ++u) {
+                        const int rq = q * kReadsPerSlot + u;
+                        if (rq < kReads) read_one(cur, s + 1, rq, fa[f ^ 1], fb[f ^ 1]);
+                    }
+                    if (s == 0) {
+#pragma unroll
+                        for (int u = 0; u < kCopiesPerSlot; ++u) {
+                            const int cq = q * kCopiesPerSlot + u;
+                            if (cq < kCopies) issue_copy(copy, cq);
+                        }
+                    }
+                } else {
+                    if (q == kHalf - 1) {
+                        __builtin_amdgcn_s_waitcnt(0);  // own copies of tile t+1 landed
+                        __syncthreads();                // ... and everyone else's
+                    }
+                    if (q >= kHalf) {
+#pragma unroll
+                        for (int u = 0; u < kReadsPerLateSlot; ++u) {
+                            const int rq = (q - kHalf) * kReadsPerLateSlot + u;
+                            if (rq < kReads) read_one(cur ^ 1, 0, rq, fa[f ^ 1], fb[f ^ 1]);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i)
-#pragma unroll
-                for (int jj = 0; jj < T::NI; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][jj],
-                                                                        acc[i][jj], 0, 0, 0);
-            constexpr int kReads = T::MI + 2 * T::NI;
-#pragma unroll
-            for (int q = 0; q < T::MI * T::NI; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
-                if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // one LDS read
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -284,11 +344,15 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
             const bool col_ok = (n0 + col) < N;
 #pragma unroll
             for (int i = 0; i < T::MI; ++i) {
+                // lane's first row of the block; register r adds
+                // 8 * (r / 4) + r % 4 rows, a wave-uniform offset
+                const int row0 = wm * T::WM + 32 * i + 4 * h;
+                const uint32_t base =
+                    col_ok ? static_cast<uint32_t>((row0 * N + col) * 4) : kOOB;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = wm * T::WM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                     const uint32_t off =
-                        col_ok ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                        base + static_cast<uint32_t>((8 * (r >> 2) + (r & 3)) * N * 4);
                     float out = alpha * acc[i][jj][r];
                     if (read_c) {
                         const float cin = __builtin_bit_cast(
@@ -305,17 +369,285 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     epilogue(beta != 0.0f);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant: 512 threads = 8 waves, two per SIMD, K step 32 and S
+// LDS stages.  The waves form two groups of four (group = wave / 4, one wave
+// of each group per SIMD) that alternate between a read phase (all MFMA
+// fragments of one K step from LDS into registers) and a compute phase (all
+// MFMAs of that K step), group 1 one phase behind group 0, with a workgroup
+// barrier between phases.  While one wave of a SIMD runs back-to-back MFMAs
+// the other issues its LDS reads, so the matrix core is not stalled by the
+// reads of the wave that feeds it (the single-wave kernel above pays for
+// every read slotted between its MFMAs).
+//
+// Global -> LDS copies run S - 1 K steps ahead.  The stage of step t+S-1 is
+// the stage of step t-1, free once both groups have read step t-1, i.e.
+// after barrier B_{2t}.  Both groups copy during their compute phases, one
+// copy after every few MFMAs (a compute phase then has no branches, and the
+// per-CU copy rate stays well below the L2 -> LDS limit of about 64 bytes
+// per clock): group 1 copies its share of step t+S-1 in its compute phase
+// of step t-1 (after B_{2t}), group 0 its share in its compute phase of step
+// t (after B_{2t+1}).  Each wave waits for its own copies of step t+1 before
+// the barrier after which step t+1 is first read (group 0 at the end of its
+// compute phase of step t, group 1 at the end of its read phase of step t):
+// copies have at least 2 S - 3 phases to land.
+//
+// LDS layouts (64-bank LDS, see the notes at the top): A stage = BM rows of
+// 32 k (64 bytes, 4 chunks), chunk c of row r at position c ^ ((r / 4) % 4),
+// so that 16 consecutive rows of one chunk cover the 64 banks; B stage = 32
+// k-rows of BN n, swizzled with swz_b as above.
+//
+// Barrier schedule (B_n = n-th barrier, T = number of K steps):
+//   all:     copy steps 0 .. S-2, wait for step 0, B_0
+//   group 1: copy its share of step S-1, B_1
+//   group 0: read(t) B_{2t+1} compute(t) B_{2t+2}            t = 0 .. T-1
+//   group 1: read(t) B_{2t+2} compute(t) B_{2t+3}            (no B after
+//            compute(T-1): both groups execute exactly 2T + 1 barriers)
+// so group 0 computes step t while group 1 reads it, and group 0 reads step
+// t+1 while group 1 computes step t.  Group 0's epilogue overlaps group 1's
+// last compute phase.
+constexpr int kPPBK = 32;
+
+template <int BM, int BN>
+struct PPTile {
+    static constexpr int WAVES_M = (BN == 256) ? 2 : 4;
+    static constexpr int WAVES_N = 8 / WAVES_M;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile
+    static constexpr int MI = WM / 32, NI = WN / 32;
+    static constexpr int A_LOADS = BM / 16 / 8;      // 1 KB copies of A per wave per step
+    static constexpr int B_ROWS = 512 / BN;          // B rows per 1 KB copy
+    static constexpr int B_LOADS = kPPBK / B_ROWS / 8;  // 1 KB copies of B per wave per step
+    static constexpr int COPIES = A_LOADS + B_LOADS;
+    static constexpr int B_CHUNKS = BN / 8;          // 16-byte chunks per B row
+    static constexpr int A_STAGE = BM * kPPBK;       // bf16 elements
+    static constexpr int B_STAGE = kPPBK * BN;
+};
+
+__device__ __forceinline__ int swz_a32(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima).
+constexpr int wait_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+
+template <int BM, int BN, int S, bool KTAIL>
+__global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, float alpha,
+                                                         float beta,
+                                                         const uint16_t *__restrict__ A,
+                                                         const uint16_t *__restrict__ B, float *C,
+                                                         int tiles_m, int tiles_n) {
+    using T = PPTile<BM, BN>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][T::A_STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][T::B_STAGE];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // ---- this wave's copies.  A copy q is wave-load L = 8 q + wave: tile
+    // rows 16 L .. 16 L + 15, lane p filling position p % 4 of row
+    // 16 L + p / 4 with logical chunk (p % 4) ^ swz_a32(row) (the key is
+    // (p / 16) % 4 for every L).  B copy q is wave-load 8 q + wave: B_ROWS
+    // rows from row B_ROWS (8 q + wave); the key of a row does not depend
+    // on q.
+    const int a_row_in = lane >> 2;
+    const int a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t a_off =
+        static_cast<uint32_t>(((16 * wave + a_row_in) * K + 8 * a_chunk) * 2);
+    const uint32_t a_step = static_cast<uint32_t>(128 * K * 2);
+    const int b_row0 = T::B_ROWS * wave + lane / T::B_CHUNKS;
+    const int b_c = (lane % T::B_CHUNKS) ^ swz_b(b_row0);
+    const bool b_ok = (n0 + 8 * b_c) < N;
+    const uint32_t b_off = static_cast<uint32_t>((b_row0 * N + 8 * b_c) * 2);
+    const uint32_t b_step = static_cast<uint32_t>(8 * T::B_ROWS * N * 2);
+
+    struct StepCopy {
+        i32x4 ra, rb;
+        uint32_t la, lb;
+        bool a_ok;
+    };
+    auto step_copy = [&](int t) {
+        const int k0 = t * kPPBK, stage = t % S;
+        StepCopy c;
+        c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                         (static_cast<long long>(M - m0) * K - k0) * 2);
+        c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                         (static_cast<long long>(K - k0) * N - n0) * 2);
+        c.a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
+        c.la = lds_address(&lds_a[stage][wave * 512]);
+        c.lb = lds_address(&lds_b[stage][wave * 512]);
+        return c;
+    };
+    auto issue_copy = [&](const StepCopy &c, int q) {
+        if (q < T::A_LOADS)
+            lds_dma16(c.ra, c.la + q * 8 * 1024, c.a_ok ? a_off + q * a_step : kOOB);
+        else
+            lds_dma16(c.rb, c.lb + (q - T::A_LOADS) * 8 * 1024,
+                      b_ok ? b_off + (q - T::A_LOADS) * b_step : kOOB);
+    };
+    auto issue_step = [&](int t) {
+        const StepCopy c = step_copy(t);
+#pragma unroll
+        for (int q = 0; q < T::COPIES; ++q) issue_copy(c, q);
+    };
+
+    // ---- fragments of one K step: A block i, k16 step s; B block jj, step s
+    const int a_lane_base = (wm * T::WM + l32) * kPPBK;
+    const int g = lane >> 4, j16 = lane & 15;
+    const int b_col_lane = wn * T::WN + 16 * (g & 1) + 4 * (j16 & 3);  // + 32 jj
+    const int b_row_lane = 8 * (g >> 1) + (j16 >> 2);                  // + 16 s + 4 r
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    constexpr int kSub = kPPBK / 16;
+    constexpr int kReads = kSub * (T::MI + 2 * T::NI);
+    bf16x8 fa[T::MI][kSub];
+    s16x8 fb[T::NI][kSub];
+    s16x4 fb_part[T::NI][kSub][2];
+    // Fragment read number q of the step (A blocks first, then B halves).
+    auto read_one = [&](int stage, int q) {
+        constexpr int per_s = T::MI + 2 * T::NI;
+        const int s = q / per_s, u = q % per_s;
+        if (u < T::MI) {
+            const int pos = ((2 * s + h) ^ swz_a32(l32)) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                &lds_a[stage][a_lane_base + 32 * u * kPPBK + pos]);
+            fa[u][s] = __builtin_bit_cast(bf16x8, v);
+        } else {
+            const int jj = (u - T::MI) >> 1, r = (u - T::MI) & 1;
+            const int row = 16 * s + 4 * r + b_row_lane;
+            const int col = b_col_lane + 32 * jj;
+            const int chunk = (col >> 3) ^ swz_b(row);
+            const int elem = row * BN + chunk * 8 + (col & 7);
+            fb_part[jj][s][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)&lds_b[stage][elem]);
+        }
+    };
+
+    f32x16 acc[T::MI][T::NI];
+#pragma unroll
+    for (int i = 0; i < T::MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < T::NI; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+
+    const int steps = (K + kPPBK - 1) / kPPBK;
+    constexpr int kWaitSteady = wait_vm(T::COPIES * (S - 2));
+    constexpr int kWaitAll = wait_vm(0);
+    for (int t = 0; t < S - 1; ++t)
+        if (t < steps) issue_step(t);
+    if (steps >= S - 1)
+        __builtin_amdgcn_s_waitcnt(kWaitSteady);  // step 0 landed
+    else
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();  // B_0
+    if (grp == 1) {
+        if (S - 1 < steps) issue_step(S - 1);
+        __syncthreads();  // B_1
+    }
+
+    constexpr int kMfma = T::MI * T::NI * kSub;
+    constexpr int kGapM = kMfma / T::COPIES;
+    // One K step: read phase, barrier, compute phase, barrier.  With COPY the
+    // compute phase also copies step t + S - 1 + grp (one copy after every
+    // kGapM-th MFMA) and the waits keep the younger steps in flight; without
+    // it (the last steps) every wait drains the queue.
+    auto k_step = [&](int t, auto copy_tag) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        const int stage = t % S;
+#pragma unroll
+        for (int q = 0; q < kReads; ++q) read_one(stage, q);
+        if (grp == 1) __builtin_amdgcn_s_waitcnt(COPY ? kWaitSteady : kWaitAll);
+        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < T::NI; ++jj)
+#pragma unroll
+            for (int s = 0; s < kSub; ++s)
+                fb[jj][s] = __builtin_shufflevector(fb_part[jj][s][0], fb_part[jj][s][1], 0, 1, 2,
+                                                    3, 4, 5, 6, 7);
+        StepCopy next;
+        if (COPY) next = step_copy(t + S - 1 + grp);
+#pragma unroll
+        for (int q = 0; q < kMfma; ++q) {
+            const int s = q / (T::MI * T::NI);
+            const int i = (q / T::NI) % T::MI, jj = q % T::NI;
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fa[i][s], __builtin_bit_cast(bf16x8, fb[jj][s]), acc[i][jj], 0, 0, 0);
+            if (COPY && q % kGapM == 0 && q / kGapM < T::COPIES) issue_copy(next, q / kGapM);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (grp == 0) {
+            __builtin_amdgcn_s_waitcnt(COPY ? kWaitSteady : kWaitAll);
+            __syncthreads();
+        } else if (t + 1 < steps) {
+            __syncthreads();
+        }
+    };
+    // Steps whose compute phase copies: group 0 copies step t + S - 1, group
+    // 1 step t + S, while that step exists.
+    const int copy_end = max(0, steps - (S - 1) - grp);
+    int t = 0;
+    for (; t < copy_end; ++t) k_step(t, std::true_type());
+    for (; t < steps; ++t) k_step(t, std::false_type());
+
+    // ---- epilogue (as in the kernel above)
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + static_cast<size_t>(m0) * N + n0,
+                  (static_cast<long long>(M - m0) * N - n0) * 4);
+    auto epilogue = [&](const bool read_c) {
+#pragma unroll
+        for (int jj = 0; jj < T::NI; ++jj) {
+            const int col = wn * T::WN + 32 * jj + l32;
+            const bool col_ok = (n0 + col) < N;
+#pragma unroll
+            for (int i = 0; i < T::MI; ++i) {
+                const int row0 = wm * T::WM + 32 * i + 4 * h;
+                const uint32_t base =
+                    col_ok ? static_cast<uint32_t>((row0 * N + col) * 4) : kOOB;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t off =
+                        base + static_cast<uint32_t>((8 * (r >> 2) + (r & 3)) * N * 4);
+                    float out = alpha * acc[i][jj][r];
+                    if (read_c) {
+                        const float cin = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(off), 0, 0));
+                        out = fmaf(beta, cin, out);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), rc,
+                                                          static_cast<int>(off), 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    epilogue(beta != 0.0f);
+}
+
 const Bf16TileConfig kConfigs[] = {
     {256, 256, "bf16_mfma_256x256x64"},
     {256, 128, "bf16_mfma_256x128x64"},
     {128, 256, "bf16_mfma_128x256x64"},
     {128, 128, "bf16_mfma_128x128x64"},
+    {256, 256, "bf16_pp_256x256x32"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-// Relative MFMA efficiency assumed for each tile (LDS bytes per MFMA grow as
-// the wave tile shrinks).
-const double kTileEfficiency[kNumConfigs] = {1.0, 0.85, 0.85, 0.5};
+// Relative per-CU speed of each tile configuration at equal occupancy,
+// measured on the square and prefill shapes (the ping-pong kernel fastest,
+// the single-wave 256-wide tiles next; the 128 x 128 tile is the unit).
+const double kTileEfficiency[kNumConfigs] = {1.2, 0.85, 0.85, 1.0, 1.27};
+// LDS bytes per workgroup, which set how many workgroups share a CU.
+int tile_lds_bytes(int c) {
+    const Bf16TileConfig &t = kConfigs[c];
+    return c == 4 ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
+}
 
 template <int BM, int BN>
 hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16_t *A,
@@ -333,6 +665,22 @@ hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16
     return hipGetLastError();
 }
 
+template <int BM, int BN, int S>
+hipError_t launch_pp(int M, int N, int K, float alpha, float beta, const uint16_t *A,
+                     const uint16_t *B, float *C, hipStream_t stream) {
+    const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(tiles)), block(512);
+    if (K % kPPBK == 0)
+        bf16_pp_kernel<BM, BN, S, false><<<grid, block, 0, stream>>>(
+            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+    else
+        bf16_pp_kernel<BM, BN, S, true><<<grid, block, 0, stream>>>(
+            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int bf16_num_tile_configs() { return kNumConfigs; }
@@ -341,16 +689,21 @@ const Bf16TileConfig &bf16_tile_config(int cfg) { return kConfigs[cfg]; }
 
 int bf16_pick_tile_config(int M, int N, int K, int num_cus) {
     (void)K;
+    // Estimated time = rounds x (workgroups sharing a CU) x tile area /
+    // efficiency, where a partial last round counts half plus its filled
+    // fraction (a half-empty round runs faster per tile: less contention).
     const int lds_per_cu = 160 * 1024;
     int best = 0;
     double best_cost = 0.0;
     for (int c = 0; c < kNumConfigs; ++c) {
         const int bm = kConfigs[c].bm, bn = kConfigs[c].bn;
         const long long wgs = static_cast<long long>((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-        const int lds = 2 * (bm + bn) * kBK * 2;
-        const long long slots = static_cast<long long>(num_cus) * (lds_per_cu / lds);
-        const long long rounds = (wgs + slots - 1) / slots;
-        const double cost = static_cast<double>(rounds) * bm * bn / kTileEfficiency[c];
+        const int occ = lds_per_cu / tile_lds_bytes(c);
+        const long long slots = static_cast<long long>(num_cus) * occ;
+        const long long full = wgs / slots, rem = wgs % slots;
+        const double rounds =
+            static_cast<double>(full) + (rem ? 0.5 + 0.5 * static_cast<double>(rem) / slots : 0.0);
+        const double cost = rounds * occ * bm * bn / kTileEfficiency[c];
         if (c == 0 || cost < best_cost) {
             best = c;
             best_cost = cost;
@@ -366,6 +719,7 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
         case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, stream);
         case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, stream);
         case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, stream);
+        case 4: return launch_pp<256, 256, 4>(M, N, K, alpha, beta, A, B, C, stream);
         default: return hipErrorInvalidValue;
     }
 }

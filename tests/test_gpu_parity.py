@@ -240,13 +240,16 @@ def test_deterministic_repeat(gpu):
 
 
 TILE_NAMES = ["bf16_mfma_256x256x64", "bf16_mfma_256x128x64", "bf16_mfma_128x256x64",
-              "bf16_mfma_128x128x64"]
+              "bf16_mfma_128x128x64", "bf16_pp_256x256x32"]
 
 
 @pytest.mark.parametrize("tile", TILE_NAMES)
-@pytest.mark.parametrize("shape", [(520, 776, 328), (256, 256, 64), (17, 296, 64)],
+@pytest.mark.parametrize("shape", [(520, 776, 328), (256, 256, 64), (17, 296, 64),
+                                   (264, 392, 1024), (260, 136, 128), (136, 520, 192)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_every_bf16_tile(tile, shape, monkeypatch):
+    """Every tile configuration: 1, 2, 3, 6 (with a K tail) and 16 K tiles,
+    ragged M and N edges."""
     monkeypatch.setenv("MGEMM_BF16_TILE", tile)
     monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
     case = make_case(*shape, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=21)
@@ -302,4 +305,4 @@ def test_dispatch_names():
         if want:
             assert name == want
         else:
-            assert name.startswith("bf16_mfma_")
+            assert name.startswith(("bf16_mfma_", "bf16_pp_"))
