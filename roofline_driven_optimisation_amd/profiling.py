@@ -26,6 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 KERNEL_SOURCES = {
     "bf16_mfma": "bf16_mfma.hip",
+    "bf16_pp": "bf16_mfma.hip",
     "f32_mfma": "f32_mfma.hip",
     "skinny": "skinny_bf16.hip",
     "naive": "naive.hip",
@@ -70,6 +71,23 @@ def kernel_stats(path: str):
     return rows
 
 
+def dispatch_stats(path: str):
+    """Per (kernel, grid size) statistics from a ``*_kernel_trace.csv``: one
+    kernel launched on several shapes shows up once per launch shape."""
+    acc = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            acc[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in acc.values())
+    rows = []
+    for (k, grid, wg), v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        rows.append({"kernel": "%s [%d workgroups x %d]" % (k, grid // max(wg, 1), wg),
+                     "calls": len(v), "avg_us": statistics.mean(v), "min_us": min(v),
+                     "max_us": max(v), "pct": 100.0 * sum(v) / total})
+    return rows
+
+
 def counter_medians(path: str):
     """{(kernel, counter): median value (KiB per dispatch)}."""
     acc = defaultdict(list)
@@ -100,6 +118,9 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats", help="markdown table from a --kernel-trace --stats run")
     s.add_argument("dir")
+    t = sub.add_parser("trace", help="markdown table per kernel and launch shape from "
+                       "--kernel-trace output")
+    t.add_argument("dir")
     c = sub.add_parser("counters", help="calibrated HBM bytes per dispatch")
     c.add_argument("--fetch", required=True, help="dir of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="dir of the WRITE_SIZE run")
@@ -109,6 +130,9 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats_markdown(kernel_stats(_find(args.dir, "_kernel_stats.csv"))))
+        return
+    if args.cmd == "trace":
+        print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"))))
         return
     fetch = counter_medians(_find(args.fetch, "_counter_collection.csv"))
     write = counter_medians(_find(args.write, "_counter_collection.csv"))
