@@ -22,7 +22,8 @@
 //     computing k), so one barrier per K step suffices;
 //   * MFMA operand fragments are double-buffered in registers: the reads for
 //     k16 sub-step s+1 are issued before the MFMAs of sub-step s;
-//   * fused alpha/beta epilogue in fp32; C is not read when beta == 0.
+//   * fused alpha/beta epilogue in fp32 with 16-byte stores (the MFMAs compute
+//     transposed blocks, see store_c_tile); C is not read when beta == 0.
 //
 // Edges.  The buffer resource's range check turns every out-of-range load
 // into zeros and drops every out-of-range store; a column or k index past the
@@ -136,6 +137,51 @@ __device__ __forceinline__ void lds_dma16(i32x4 desc, uint32_t lds_addr, uint32_
 
 __device__ __forceinline__ uint32_t lds_address(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p));
+}
+
+// Epilogue of one wave: C = alpha * acc + beta * C for MI x NI blocks of 32 x
+// 32.  The MFMAs take the B fragment as their first operand and the A
+// fragment as their second, so each block holds the transposed product: in
+// register r of lane l sits C[row l % 32][column 8 (r / 4) + 4 (l / 32) +
+// r % 4] of the block, i.e. registers 4 g .. 4 g + 3 are four consecutive
+// columns, written (and, with beta != 0, read) as one 16-byte access.  The
+// descriptor `rc` is based at the workgroup tile origin and ends at the last
+// element of C, so rows past M fall outside it; a 4-column group past N
+// (N is a multiple of 8, so a group is entirely inside or outside) is
+// redirected out of range.  Stores of one block are issued before the next
+// block is converted, which bounds the registers in use.
+template <int MI, int NI>
+__device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
+                                             __amdgpu_buffer_rsrc_t rc, int row0, int col0,
+                                             int cols_left, int N, float alpha, float beta) {
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, h = lane >> 5;
+    const bool read_c = beta != 0.0f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj) {
+            const int row = row0 + 32 * i + l32;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = col0 + 32 * jj + 8 * g + 4 * h;
+                const uint32_t off =
+                    col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = alpha * acc[i][jj][4 * g + e];
+                if (read_c) {
+                    const f32x4 cin = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
+                                                       static_cast<int>(off), 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 template <int BM, int BN, bool KTAIL>
@@ -299,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
             for (int q = 0; q < kMfma; ++q) {
                 const int i = q / T::NI, jj = q % T::NI;
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    fa[f][i], __builtin_bit_cast(bf16x8, fb[f][jj]), acc[i][jj], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, fb[f][jj]), fa[f][i], acc[i][jj], 0, 0, 0);
                 if (!last) {
 #pragma unroll
                     for (int u = 0; u < kReadsPerSlot; ++u) {
@@ -331,42 +377,11 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
         }
     }
 
-    // ---- epilogue: register r of a 32 x 32 block is row 8*(r/4) + 4*h + r%4,
-    // column l32; rows past M fall outside the descriptor, columns past N are
-    // redirected out of range.
+    // ---- epilogue
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
-    auto epilogue = [&](const bool read_c) {
-#pragma unroll
-        for (int jj = 0; jj < T::NI; ++jj) {
-            const int col = wn * T::WN + 32 * jj + l32;
-            const bool col_ok = (n0 + col) < N;
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i) {
-                // lane's first row of the block; register r adds
-                // 8 * (r / 4) + r % 4 rows, a wave-uniform offset
-                const int row0 = wm * T::WM + 32 * i + 4 * h;
-                const uint32_t base =
-                    col_ok ? static_cast<uint32_t>((row0 * N + col) * 4) : kOOB;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const uint32_t off =
-                        base + static_cast<uint32_t>((8 * (r >> 2) + (r & 3)) * N * 4);
-                    float out = alpha * acc[i][jj][r];
-                    if (read_c) {
-                        const float cin = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(off), 0, 0));
-                        out = fmaf(beta, cin, out);
-                    }
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), rc,
-                                                          static_cast<int>(off), 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded registers
-            }
-        }
-    };
-    epilogue(beta != 0.0f);
+    store_c_tile<T::MI, T::NI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,7 +593,7 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
             const int s = q / (T::MI * T::NI);
             const int i = (q / T::NI) % T::MI, jj = q % T::NI;
             acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                fa[i][s], __builtin_bit_cast(bf16x8, fb[jj][s]), acc[i][jj], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, fb[jj][s]), fa[i][s], acc[i][jj], 0, 0, 0);
             if (COPY && q % kGapM == 0 && q / kGapM < T::COPIES) issue_copy(next, q / kGapM);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -596,38 +611,11 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     for (; t < copy_end; ++t) k_step(t, std::true_type());
     for (; t < steps; ++t) k_step(t, std::false_type());
 
-    // ---- epilogue (as in the kernel above)
+    // ---- epilogue
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
-    auto epilogue = [&](const bool read_c) {
-#pragma unroll
-        for (int jj = 0; jj < T::NI; ++jj) {
-            const int col = wn * T::WN + 32 * jj + l32;
-            const bool col_ok = (n0 + col) < N;
-#pragma unroll
-            for (int i = 0; i < T::MI; ++i) {
-                const int row0 = wm * T::WM + 32 * i + 4 * h;
-                const uint32_t base =
-                    col_ok ? static_cast<uint32_t>((row0 * N + col) * 4) : kOOB;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const uint32_t off =
-                        base + static_cast<uint32_t>((8 * (r >> 2) + (r & 3)) * N * 4);
-                    float out = alpha * acc[i][jj][r];
-                    if (read_c) {
-                        const float cin = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(off), 0, 0));
-                        out = fmaf(beta, cin, out);
-                    }
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, out), rc,
-                                                          static_cast<int>(off), 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    };
-    epilogue(beta != 0.0f);
+    store_c_tile<T::MI, T::NI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta);
 }
 
 const Bf16TileConfig kConfigs[] = {

@@ -41,14 +41,14 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
 // Skinny-M (M <= 16) bf16 kernel that streams B once from HBM.  Needs
 // K % 8 == 0, N % 8 == 0 and 16-byte aligned A, B and C.  With splits > 1 the
 // K range is divided over `splits` workgroups per column block, which reduce
-// through `partials` (splits * M * N floats) and `counters` (one int per
-// column block, zero on entry and left zero on exit); both must live in
-// uncached device memory (hipDeviceMallocUncached).
+// through `partials` (splits * M * N floats) and `counters` (`counter_ints`
+// ints, at least one per column block, zero on entry and left zero on
+// exit); both must live in uncached device memory (hipDeviceMallocUncached).
 constexpr int kSkinnyMaxM = 16;
 constexpr int kSkinnyCols = 128;  // output columns per workgroup
 int skinny_pick_splits(int M, int N, int K, int num_cus);
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
-                              int *counters, hipStream_t stream);
+                              int *counters, int counter_ints, hipStream_t stream);
 
 }  // namespace mgemm

@@ -9,9 +9,13 @@
 //
 // Work split.  A workgroup (4 waves) owns 128 output columns and a slice of
 // K; the slices of one column block are `splits` workgroups, so the grid has
-// (N / 128) * splits workgroups and fills all 256 CUs even when N = 4096.
-// Inside a workgroup the waves take turns over 32-row k-blocks, two at a
-// time, so each lane has sixteen 16-byte loads in flight.
+// (N / 128) * splits workgroups.  One CU alone cannot keep enough loads in
+// flight to draw more than a few tens of GB/s, so the grid is sized to a few
+// workgroups per CU over all 256 CUs.  Inside a workgroup the waves take
+// turns over 32-row k-blocks.  The loop is software-pipelined two k-blocks
+// deep: the sixteen 16-byte loads of the next pair of k-blocks are issued
+// before the current pair is multiplied, so every lane keeps 16 to 32 loads
+// in flight the whole time, not just between compute bursts.
 //
 // Per k-block, lane l loads eight B rows (k = 32 kb + 8 (l / 16) + e) at
 // columns 8 (l % 16) .. +7: sixteen lanes read 256 contiguous bytes of a row.
@@ -48,73 +52,124 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKBlock = 32;  // k rows per MFMA step
-constexpr int kUnroll = 2;   // k-blocks in flight per wave
+constexpr int kDepth = 1;    // k-blocks per pipeline stage
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every descriptor range
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;         // buffer-load cache policy: streaming (nt)
+constexpr int kCounterLine = 32;        // ints per 128-byte line
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, long long bytes) {
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcFlags);
+}
+
+// The loads of one pipeline stage: kDepth k-blocks, each 8 B rows and one
+// A octet per lane.
+struct Stage {
+    u32x4 b[kDepth][8];
+    u32x4 a[kDepth];
+};
 
 __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, float alpha,
                                                           float beta,
                                                           const uint16_t *__restrict__ A,
                                                           const uint16_t *__restrict__ B,
                                                           float *C, int splits, int kblk_per_split,
-                                                          float *partials, int *counters) {
+                                                          float *partials, int *counters,
+                                                          int counter_stride) {
     __shared__ f32x4 red[kWaves][8][64];
     __shared__ int s_last;
 
     const int cb = blockIdx.x / splits;
     const int sp = blockIdx.x - cb * splits;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4;      // k-octet inside a 32-row k-block
     const int cg = lane & 15;     // 8-column group inside the 128-column block
-    const int n = cb * kSkinnyCols + cg * 8;
-    const bool n_ok = n < N;
     const int m_a = lane & 15;    // row of A this lane feeds to the MFMA
-    const bool m_ok = m_a < M;
 
     const int total_kblk = (K + kKBlock - 1) / kKBlock;
     const int kb_begin = sp * kblk_per_split;
     const int kb_end = min(kb_begin + kblk_per_split, total_kblk);
+    // k-blocks of this wave: kb_begin + wave + 4 j, j = 0 .. nj - 1
+    const int nj = max(0, (kb_end - kb_begin - wave + kWaves - 1) / kWaves);
+    const int stages = (nj + kDepth - 1) / kDepth;
+
+    // Buffer descriptors based at the slice origin (row kb_begin * 32 of B,
+    // column cb * 128; column kb_begin * 32 of A), so that every offset used
+    // fits in 32 bits.  Rows past the slice or past K, columns past N and
+    // rows of A past M are given the out-of-range offset and read as zeros.
+    const long long k_first = static_cast<long long>(kb_begin) * kKBlock;
+    const __amdgpu_buffer_rsrc_t rb = rsrc(
+        B + k_first * N + static_cast<long long>(cb) * kSkinnyCols,
+        ((K - k_first) * N - static_cast<long long>(cb) * kSkinnyCols) * 2);
+    const __amdgpu_buffer_rsrc_t ra =
+        rsrc(A + k_first, (static_cast<long long>(M) * K - k_first) * 2);
+    const int k_slice = (kb_end - kb_begin) * kKBlock;  // rows of B in this slice (<= K - k_first)
+    const bool n_ok = cb * kSkinnyCols + cg * 8 < N;
+    const bool m_ok = m_a < M;
+    // row r (within the slice) of lane's B column group; k of A for this lane
+    auto b_off = [&](int r) -> uint32_t {
+        return (n_ok && r < k_slice && r + static_cast<int>(k_first) < K)
+                   ? static_cast<uint32_t>((r * N + cg * 8) * 2) : kOOB;
+    };
+    auto a_off = [&](int kk) -> uint32_t {
+        return (m_ok && kk < k_slice && kk + static_cast<int>(k_first) < K)
+                   ? static_cast<uint32_t>((m_a * K + kk) * 2) : kOOB;
+    };
+
+    auto load_stage = [&](int st, Stage &x) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int j = st * kDepth + d;
+            const int r0 = (j < nj) ? (wave + kWaves * j) * kKBlock + q * 8 : k_slice;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x.b[d][e] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, static_cast<int>(b_off(r0 + e)),
+                                                                 0, kNonTemporal));
+            x.a[d] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, static_cast<int>(a_off(r0)), 0, 0));
+        }
+    };
 
     f32x4 acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = kb_begin + wave; kb < kb_end; kb += kWaves * kUnroll) {
-        u32x4 rb[kUnroll][8];
-        u32x4 ra[kUnroll];
+    auto compute_stage = [&](const Stage &x) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int kbu = kb + u * kWaves;
-            const bool blk_ok = kbu < kb_end;
-            const int k0 = kbu * kKBlock + q * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (blk_ok && n_ok && k0 + e < K)
-                    v = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(B + static_cast<size_t>(k0 + e) * N + n));
-                rb[u][e] = v;
-            }
-            u32x4 a = {0u, 0u, 0u, 0u};
-            if (blk_ok && m_ok && k0 < K)
-                a = *reinterpret_cast<const u32x4 *>(A + static_cast<size_t>(m_a) * K + k0);
-            ra[u] = a;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bf16x8 a = as_bf16x8(ra[u]);
+        for (int d = 0; d < kDepth; ++d) {
+            const bf16x8 a = as_bf16x8(x.a[d]);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 // column t of the 8 x 8 block as eight k-consecutive bf16
-                const int d = t >> 1;
+                const int w2 = t >> 1;
                 u32x4 col;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    col[w] = (t & 1) ? pack_hi(rb[u][2 * w][d], rb[u][2 * w + 1][d])
-                                     : pack_lo(rb[u][2 * w][d], rb[u][2 * w + 1][d]);
+                    col[w] = (t & 1) ? pack_hi(x.b[d][2 * w][w2], x.b[d][2 * w + 1][w2])
+                                     : pack_lo(x.b[d][2 * w][w2], x.b[d][2 * w + 1][w2]);
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(col), acc[t], 0, 0, 0);
             }
+        }
+    };
+
+    // Two register stages: the loads of stage s+1 are in flight while stage
+    // s is multiplied.
+    Stage x0, x1;
+    if (stages > 0) load_stage(0, x0);
+    for (int st = 0; st < stages; st += 2) {
+        if (st + 1 < stages) load_stage(st + 1, x1);
+        compute_stage(x0);
+        if (st + 1 < stages) {
+            if (st + 2 < stages) load_stage(st + 2, x0);
+            compute_stage(x1);
         }
     }
 
@@ -137,51 +192,8 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
         v[t] = s;
     }
 
-    if (splits == 1) {
-        if (ok) {
-            float *c = C + static_cast<size_t>(m) * N + nn;
-            f32x4 o0, o1;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                o0[t] = alpha * v[t];
-                o1[t] = alpha * v[t + 4];
-            }
-            if (beta != 0.0f) {
-                const f32x4 c0 = reinterpret_cast<const f32x4 *>(c)[0];
-                const f32x4 c1 = reinterpret_cast<const f32x4 *>(c)[1];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    o0[t] = fmaf(beta, c0[t], o0[t]);
-                    o1[t] = fmaf(beta, c1[t], o1[t]);
-                }
-            }
-            reinterpret_cast<f32x4 *>(c)[0] = o0;
-            reinterpret_cast<f32x4 *>(c)[1] = o1;
-        }
-        return;
-    }
-
-    if (ok) {
-        f32x4 *p = reinterpret_cast<f32x4 *>(partials + (static_cast<size_t>(sp) * M + m) * N + nn);
-        p[0] = f32x4{v[0], v[1], v[2], v[3]};
-        p[1] = f32x4{v[4], v[5], v[6], v[7]};
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counters[cb], 1) == splits - 1);
-    __syncthreads();
-    if (!s_last) return;
-
-    if (ok) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) {
-            const f32x4 *p =
-                reinterpret_cast<const f32x4 *>(partials + (static_cast<size_t>(s) * M + m) * N + nn);
-            s0 += p[0];
-            s1 += p[1];
-        }
+    auto store_c = [&](f32x4 o0, f32x4 o1) {
         float *c = C + static_cast<size_t>(m) * N + nn;
-        f32x4 o0 = alpha * s0, o1 = alpha * s1;
         if (beta != 0.0f) {
             const f32x4 c0 = reinterpret_cast<const f32x4 *>(c)[0];
             const f32x4 c1 = reinterpret_cast<const f32x4 *>(c)[1];
@@ -193,18 +205,68 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
         }
         reinterpret_cast<f32x4 *>(c)[0] = o0;
         reinterpret_cast<f32x4 *>(c)[1] = o1;
+    };
+
+    if (splits == 1) {
+        if (ok)
+            store_c(alpha * f32x4{v[0], v[1], v[2], v[3]}, alpha * f32x4{v[4], v[5], v[6], v[7]});
+        return;
     }
-    if (tid == 0) atomicExch(&counters[cb], 0);  // re-arm for the next call
+
+    // one counter per column block, each on its own 128-byte line when the
+    // counter block has room (atomics on one line are serialised)
+    int *counter = counters + cb * counter_stride;
+    if (ok) {
+        f32x4 *p = reinterpret_cast<f32x4 *>(partials + (static_cast<size_t>(sp) * M + m) * N + nn);
+        p[0] = f32x4{v[0], v[1], v[2], v[3]};
+        p[1] = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(counter, 1) == splits - 1);
+    __syncthreads();
+    if (!s_last) return;
+
+    if (ok) {
+        // Eight splits' partials are requested at a time and then added in
+        // split order: one memory round trip per eight splits, and the same
+        // summation order on every call.
+        constexpr int kBatch = 8;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        for (int sb = 0; sb < splits; sb += kBatch) {
+            f32x4 p0[kBatch], p1[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int s = min(sb + u, splits - 1);
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(
+                    partials + (static_cast<size_t>(s) * M + m) * N + nn);
+                p0[u] = p[0];
+                p1[u] = p[1];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (sb + u < splits) {
+                    s0 += p0[u];
+                    s1 += p1[u];
+                }
+            }
+        }
+        store_c(alpha * s0, alpha * s1);
+    }
+    if (tid == 0) atomicExch(counter, 0);  // re-arm for the next call
 }
 
 }  // namespace
 
 int skinny_pick_splits(int M, int N, int K, int num_cus) {
     (void)M;
+    // Measured on the decode shapes (4096 x 11008, 11008 x 4096, 4096 x
+    // 32000): eight splits, i.e. 256 to 2000 workgroups, is at or near the
+    // best everywhere; fewer column blocks than CUs raise the count so that
+    // every CU streams.
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
-    const int target = num_cus + num_cus / 4;  // about 1.25 workgroups per CU (measured best)
-    int splits = (target + col_blocks - 1) / col_blocks;
+    int splits = max(8, (num_cus + col_blocks - 1) / col_blocks);
     const int max_splits = kblks / 8 > 1 ? kblks / 8 : 1;  // >= 8 k-blocks per workgroup
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
@@ -213,19 +275,25 @@ int skinny_pick_splits(int M, int N, int K, int num_cus) {
 
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
-                              int *counters, hipStream_t stream) {
+                              int *counters, int counter_ints, hipStream_t stream) {
     if (M < 1 || M > kSkinnyMaxM || splits < 1) return hipErrorInvalidValue;
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
     int per = (kblks + splits - 1) / splits;
     if (per < 1) per = 1;
+    // 32-bit buffer offsets: one slice of B and all of A must stay below 2^31 bytes
+    if (static_cast<long long>(per) * kKBlock * N * 2 >= 0x7fff0000LL ||
+        static_cast<long long>(M) * K * 2 >= 0x7fff0000LL)
+        return hipErrorInvalidValue;
     // recompute so that no split is empty: each one must arrive at the counter
     const int real_splits = (kblks + per - 1) / per > 0 ? (kblks + per - 1) / per : 1;
     if (real_splits > 1 && (partials == nullptr || counters == nullptr)) return hipErrorInvalidValue;
     const long long grid = static_cast<long long>(col_blocks) * real_splits;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int counter_stride = col_blocks * kCounterLine <= counter_ints ? kCounterLine : 1;
+    if (real_splits > 1 && col_blocks > counter_ints) return hipErrorInvalidValue;
     skinny_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
-        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters);
+        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters, counter_stride);
     return hipGetLastError();
 }
 
