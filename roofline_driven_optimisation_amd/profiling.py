@@ -89,11 +89,15 @@ def dispatch_stats(path: str):
 
 
 def counter_medians(path: str):
-    """{(kernel, counter): median value (KiB per dispatch)}."""
+    """{(kernel, counter): median value (KiB per dispatch)}; a kernel launched
+    on several shapes is keyed as 'name [W workgroups]' per launch shape."""
     acc = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
-            acc[(short_name(r["Kernel_Name"]), r["Counter_Name"])].append(float(r["Counter_Value"]))
+            wg = max(int(r.get("Workgroup_Size", 1) or 1), 1)
+            grid = int(r.get("Grid_Size", 0) or 0)
+            name = "%s [%d workgroups]" % (short_name(r["Kernel_Name"]), grid // wg)
+            acc[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
     return {k: statistics.median(v) for k, v in acc.items()}
 
 
@@ -147,7 +151,7 @@ def main():
         w = write.get((k, "WRITE_SIZE"), float("nan"))
         fb, wb = v * 1024 * f_fac, w * 1024 * w_fac
         print("%s: fetch %.1f MB, write %.1f MB, total %.1f MB per dispatch (source %s)"
-              % (k, fb / 1e6, wb / 1e6, (fb + wb) / 1e6, source_hash(k)))
+              % (k, fb / 1e6, wb / 1e6, (fb + wb) / 1e6, source_hash(k.split("<")[0])))
 
 
 if __name__ == "__main__":
