@@ -273,6 +273,23 @@ def test_skinny_splits(splits, shape, monkeypatch):
     check_full(case, C)
 
 
+def test_skinny_workspace_reuse(monkeypatch):
+    """Consecutive split-K calls on one stream with different shapes and split
+    counts share one workspace: each call must find every slot re-armed by the
+    call before it (exact match on integer inputs, every call)."""
+    plan = [((16, 4096, 2048), 8), ((1, 520, 4096), 3), ((16, 1032, 8192), 24),
+            ((7, 4096, 1024), 2), ((16, 4096, 2048), 8), ((1, 136, 512), 16),
+            ((16, 1032, 8192), 5)]
+    for rep in range(2):
+        for i, (shape, splits) in enumerate(plan):
+            monkeypatch.setenv("MGEMM_SKINNY_SPLITS", str(splits))
+            case = make_case(*shape, "bf16", 1.0, 0.5, "i:4", "i:4", "i:4", seed=40 + i)
+            C, name = run(case)
+            assert name == "skinny_bf16_splitk", (shape, splits, name)
+            Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.0, 0.5, bf16=True)
+            assert np.array_equal(C.astype(np.float64), Cref), (rep, shape, splits)
+
+
 @pytest.mark.parametrize("M", list(range(1, 18)) + [31, 32, 33])
 def test_skinny_boundary(M):
     """Every M around the skinny threshold (<= 16 skinny, above tiled)."""
