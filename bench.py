@@ -13,8 +13,14 @@ by device synchronisations.  The same line carries:
 * ``also``: the other workloads (fp32 4096^3 and 4092^3 with alpha 1.5 and
   beta 0.5, LLaMA-7B prefill projections, decode-shaped GEMMs) with TFLOP/s,
   algorithmic GB/s and their own roofline fraction;
+* ``ladder``: the one-thread-per-output kernel against the tiled one on
+  fp32 4092^3, the first and last rungs of the optimisation ladder;
+* ``page_context``: the figures the pages quote for other machines;
 * ``cpu_baseline``: the CPU oracle, as it stands, timed on a bounded sample
   of the headline workload (rank 0, N = 1 only).
+
+``--sustain SECONDS`` instead launches a workload back to back and samples
+the GFX clock and board power with amd-smi (the GEMM runs at the power limit).
 
 Every timed launch cycles through several copies of the operands whose total
 exceeds twice the 256 MB last-level cache, so each launch streams from HBM.
@@ -97,10 +103,14 @@ class Prepared:
         self.C0 = C.clone() if case.C is not None else None
         self.rf = rl.gemm_roofline(case.M, case.N, case.K, case.dtype, case.beta != 0.0)
 
-    def launch(self, i: int):
+    def launch(self, i: int, naive: bool = False):
         from roofline_driven_optimisation_amd import binding
         A, B, C = self.bufs[i % self.sets]
-        binding.gemm(A, B, C, self.w.alpha, self.w.beta)
+        if naive:
+            fn = binding.gemm_naive_bf16 if self.case.bf16 else binding.gemm_naive_f32
+            fn(A, B, C, self.w.alpha, self.w.beta)
+        else:
+            binding.gemm(A, B, C, self.w.alpha, self.w.beta)
 
     def kernel_name(self) -> str:
         from roofline_driven_optimisation_amd import binding
@@ -108,18 +118,18 @@ class Prepared:
         return binding.last_kernel()
 
 
-def time_workload(p: Prepared, steps: int, warmup: int):
+def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
     """(wall seconds per step, event seconds per launch) over `steps` launches."""
     import torch
     for i in range(warmup):
-        p.launch(i)
+        p.launch(i, naive)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        p.launch(i)
+        p.launch(i, naive)
     end.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
@@ -137,6 +147,94 @@ def summary(p: Prepared, sec: float, kname: str) -> dict:
         "roofline_tflops": round(p.rf.attainable / 1e12, 1),
         "frac": round(p.rf.fraction(sec), 4),
     }
+
+
+# Figures the pages quote, for context only (other machines; no MI355X number
+# exists in them, so vs_baseline stays null).
+PAGE_CONTEXT = {
+    "rtx_a6000_fp32_4092": {"naive_row_major_gflops": 309, "naive_coalesced_gflops": 1986,
+                            "cublas_gflops": 23250, "source": "Boehm SGEMM worklog, as quoted"},
+    "h100_sxm5_spec": {"fp32_tflops": 67, "bf16_dense_tflops": 989, "hbm_tbs": 3.35},
+}
+
+
+def naive_ladder(steps: int = 3) -> dict:
+    """The first rung of the optimisation ladder: one thread per output, no
+    data reuse beyond the caches, on fp32 4092^3 (alpha 1.5, beta 0.5), next
+    to the tiled kernel on the same workload."""
+    p = Prepared("f32_4092")
+    _, naive_s = time_workload(p, steps, 1, naive=True)
+    _, tiled_s = time_workload(p, 20, 3)
+    out = {"workload": "f32_4092", "naive_us": round(naive_s * 1e6, 1),
+           "naive_tflops": round(p.rf.flops / naive_s / 1e12, 2),
+           "tiled_us": round(tiled_s * 1e6, 1),
+           "tiled_tflops": round(p.rf.flops / tiled_s / 1e12, 2),
+           "speedup": round(naive_s / tiled_s, 1)}
+    del p
+    return out
+
+
+def sample_smi():
+    """One amd-smi reading of the GFX clock (XCD 0) and socket power, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power"],
+                           capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    clk = re.search(r"GFX_0:\s*\n\s*CLK:\s*([0-9.]+)", r.stdout)
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)", r.stdout)
+    if not clk or not pw:
+        return None
+    return {"gfx0_clock_mhz": float(clk.group(1)), "socket_power_w": float(pw.group(1))}
+
+
+def sustain(name: str, seconds: float) -> dict:
+    """Launch one workload back to back for `seconds` while amd-smi samples the
+    clock and board power (steady state: power- and thermally-settled)."""
+    import threading
+    import torch
+    p = Prepared(name)
+    kname = p.kernel_name()
+    samples = []
+
+    def sampler():
+        time.sleep(min(1.0, seconds / 4))
+        while not done.is_set():
+            s = sample_smi()
+            if s:
+                samples.append(s)
+            done.wait(0.5)
+
+    done = threading.Event()
+    th = threading.Thread(target=sampler)
+    th.start()
+    n = 0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    while time.perf_counter() - t0 < seconds:
+        for i in range(100):
+            p.launch(n + i)
+        n += 100
+        torch.cuda.synchronize()
+    end.record()
+    torch.cuda.synchronize()
+    done.set()
+    th.join()
+    sec = start.elapsed_time(end) * 1e-3 / n
+    return {"workload": name, "kernel": kname, "launches": n, "us": round(sec * 1e6, 2),
+            "tflops": round(p.rf.flops / sec / 1e12, 2), "smi_samples": samples}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(budget_s: float = 12.0) -> dict:
@@ -158,7 +256,8 @@ def cpu_baseline(budget_s: float = 12.0) -> dict:
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "rows 0..%d of the bf16 4096^3 GEMM (%dx4096 outputs, K=4096), "
-                      "fp64 i-k-j loop, %.1f s" % (rows - 1, rows, t)}
+                      "fp64 i-k-j loop, %.1f s" % (rows - 1, rows, t),
+            "cpu": cpu_model(), "logical_cpus": os.cpu_count()}
 
 
 def main():
@@ -170,6 +269,11 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated workloads to time "
                     "(profiling runs); skips the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ladder", action="store_true",
+                    help="skip the naive-kernel rung (fp32 4092^3)")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="only launch the --only workloads (default: the headline) back to "
+                    "back for SECONDS each, sampling clock and power with amd-smi")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times "
                     "(calibrates the HBM byte counters)")
@@ -200,6 +304,11 @@ def main():
                         "gbs_read_plus_write": round(2 * n / sec / 1e9, 1)}))
         return
 
+    if args.sustain > 0:
+        for name in (args.only or HEADLINE).split(","):
+            log(json.dumps(sustain(name, args.sustain)))
+        return
+
     if args.only:
         for name in args.only.split(","):
             p = Prepared(name)
@@ -226,6 +335,12 @@ def main():
         del p
         torch.cuda.empty_cache()
 
+    ladder = None
+    if not args.no_ladder:
+        log("bench: naive rung, fp32 4092^3")
+        ladder = naive_ladder()
+        log("  " + json.dumps(ladder))
+
     traffic = stored_traffic(kname, HEADLINE)
     achieved = head.rf.flops / ev / 1e12
     peak = rl.MI355X_PEAK_BF16 / 1e12
@@ -249,6 +364,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "also": also,
+        "ladder": ladder,
+        "page_context": PAGE_CONTEXT,
     }
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")

@@ -101,6 +101,52 @@ def counter_medians(path: str):
     return {k: statistics.median(v) for k, v in acc.items()}
 
 
+NUM_XCD = 8          # GRBM counters are summed over the XCDs
+NUM_SIMD = 256 * 4   # MFMA busy cycles are summed over every SIMD
+SPEC_CLOCK_GHZ = 2.4
+MOPS_FLOP = 512      # one MFMA "MOP" is 512 floating-point operations
+
+
+def mfma_rows(path: str):
+    """Per kernel and launch shape, from one --pmc pass with GRBM_GUI_ACTIVE,
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_* (medians over
+    dispatches): duration, average shader clock, share of SIMD cycles the
+    matrix cores were busy, and the MFMA FLOPs counted."""
+    acc = defaultdict(lambda: defaultdict(list))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            wg = max(int(r.get("Workgroup_Size", 1) or 1), 1)
+            grid = int(r.get("Grid_Size", 0) or 0)
+            name = "%s [%d workgroups]" % (short_name(r["Kernel_Name"]), grid // wg)
+            acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                acc[name]["_ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    rows = []
+    for name, c in sorted(acc.items()):
+        if "GRBM_GUI_ACTIVE" not in c or not any(c["SQ_VALU_MFMA_BUSY_CYCLES"]):
+            continue
+        med = {k: statistics.median(v) for k, v in c.items()}
+        cycles = med["GRBM_GUI_ACTIVE"] / NUM_XCD
+        ns = med["_ns"]
+        mops = sum(v for k, v in med.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
+        rows.append({"kernel": name, "us": ns / 1e3, "clock_ghz": cycles / ns,
+                     "mfma_busy": med["SQ_VALU_MFMA_BUSY_CYCLES"] / (NUM_SIMD * cycles),
+                     "mfma_gflop": mops * MOPS_FLOP / 1e9,
+                     "mfma_tflops": mops * MOPS_FLOP / ns / 1e3})
+    return rows
+
+
+def mfma_markdown(rows) -> str:
+    out = ["| kernel | us | avg clock GHz | MFMA busy (of SIMD cycles) | MFMA GFLOP counted | "
+           "TFLOP/s from counters | share of spec (busy x clock / 2.4 GHz) |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %s | %.1f | %.2f | %.1f %% | %.1f | %.1f | %.1f %% |" % (
+            r["kernel"], r["us"], r["clock_ghz"], 100 * r["mfma_busy"], r["mfma_gflop"],
+            r["mfma_tflops"], 100 * r["mfma_busy"] * r["clock_ghz"] / SPEC_CLOCK_GHZ))
+    return "\n".join(out)
+
+
 def stats_markdown(rows) -> str:
     out = ["| kernel | calls | avg us | min us | max us | % of GPU time |",
            "|---|---|---|---|---|---|"]
@@ -125,6 +171,9 @@ def main():
     t = sub.add_parser("trace", help="markdown table per kernel and launch shape from "
                        "--kernel-trace output")
     t.add_argument("dir")
+    m = sub.add_parser("mfma", help="clock and matrix-core utilisation from a --pmc pass "
+                       "with GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_*")
+    m.add_argument("dir")
     c = sub.add_parser("counters", help="calibrated HBM bytes per dispatch")
     c.add_argument("--fetch", required=True, help="dir of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="dir of the WRITE_SIZE run")
@@ -134,6 +183,9 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats_markdown(kernel_stats(_find(args.dir, "_kernel_stats.csv"))))
+        return
+    if args.cmd == "mfma":
+        print(mfma_markdown(mfma_rows(_find(args.dir, "_counter_collection.csv"))))
         return
     if args.cmd == "trace":
         print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"))))
