@@ -18,11 +18,23 @@
 // and without packed fp32 math the VALU reaches only half of it, so the matrix
 // core is the only way to the fp32 roofline here.
 //
-// LDS layout: A is stored transposed, As[k][m], so that the MFMA A operand
-// (lane l reads row l % 32 at k = l / 32) is a conflict-free 32-float row
-// read; B stays Bs[k][n] as it comes from global memory.  Rows are padded by 4
-// floats.  Out-of-range rows and columns are zero-filled on load and never
-// stored (the edge handling of section 10.6 of the same page).
+// LDS layouts (64 four-byte banks; a wave's 64 single-float fragment reads
+// must touch 64 distinct banks).  Both tiles keep their global layout:
+//   * A as As[m][k], rows of 32 floats padded to 34: lane (m, h) reads
+//     As[m][2 s + h]; the bank is (34 m + 2 s + h) mod 64, and 34 m mod 64 is
+//     2 m for even m and 2 m + 32 for odd m, so the 64 lanes hit 64 banks.
+//     A row segment is written as two 8-byte stores (rows are 8-byte aligned);
+//   * B as Bs[k][n], rows of 128 floats padded to 160: lanes h = 0 and h = 1
+//     read rows 2 s and 2 s + 1, 160 floats = 32 banks apart, so the two
+//     halves of the wave cover disjoint banks; rows are written with 16-byte
+//     stores.
+// Out-of-range rows and columns are zero-filled on load and never stored
+// (the edge handling of section 10.6 of the same page).
+//
+// The MFMAs take the B fragment as their first operand and the A fragment as
+// their second, so each 32 x 32 block holds the transposed product: register
+// r of lane l is C[row l % 32][column 8 (r / 4) + 4 (l / 32) + r % 4], and
+// the epilogue reads and writes C in 16-byte pieces.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,9 +43,8 @@ namespace mgemm {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kPad = 4;
-constexpr int kLdA = kBM + kPad;  // floats per As row (one k)
-constexpr int kLdB = kBN + kPad;  // floats per Bs row (one k)
+constexpr int kLdA = kBK + 2;   // floats per As row (one m)
+constexpr int kLdB = kBN + 32;  // floats per Bs row (one k)
 constexpr int kThreads = 256;
 constexpr int kAChunks = kBM * kBK / 4 / kThreads;  // float4 chunks of A per thread (4)
 constexpr int kBChunks = kBK * kBN / 4 / kThreads;  // float4 chunks of B per thread (4)
@@ -61,8 +72,8 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
                                                                const float *__restrict__ B,
                                                                float *C, int tiles_m,
                                                                int tiles_n) {
-    __shared__ float As[2][kBK][kLdA];
-    __shared__ float Bs[2][kBK][kLdB];
+    __shared__ __attribute__((aligned(16))) float As[2][kBM][kLdA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kBK][kLdB];
 
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tm, tn);
@@ -98,10 +109,9 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
         for (int i = 0; i < kAChunks; ++i) {
             const int c = tid + kThreads * i;
             const int r = c >> 3, kq = (c & 7) * 4;
-            As[buf][kq + 0][r] = ra[i].x;
-            As[buf][kq + 1][r] = ra[i].y;
-            As[buf][kq + 2][r] = ra[i].z;
-            As[buf][kq + 3][r] = ra[i].w;
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<f32x2 *>(&As[buf][r][kq]) = f32x2{ra[i].x, ra[i].y};
+            *reinterpret_cast<f32x2 *>(&As[buf][r][kq + 2]) = f32x2{ra[i].z, ra[i].w};
         }
 #pragma unroll
         for (int i = 0; i < kBChunks; ++i) {
@@ -129,34 +139,53 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
 #pragma unroll
         for (int s = 0; s < kBK / 2; ++s) {
             const int kk = 2 * s + h;
-            const float a0 = As[cur][kk][wm * 64 + l32];
-            const float a1 = As[cur][kk][wm * 64 + 32 + l32];
+            const float a0 = As[cur][wm * 64 + l32][kk];
+            const float a1 = As[cur][wm * 64 + 32 + l32][kk];
             const float b0 = Bs[cur][kk][wn * 64 + l32];
             const float b1 = Bs[cur][kk][wn * 64 + 32 + l32];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[1][1], 0, 0, 0);
         }
         if (t + 1 < ktiles) store_tile(cur ^ 1);
         __syncthreads();
     }
 
-    // Epilogue.  Accumulator register r of a 32 x 32 block holds row
-    // 8 * (r / 4) + 4 * (lane / 32) + r % 4 and column lane % 32.
+    // Epilogue: block (i, j) register 4 g + e of lane l is C[row][col + e]
+    // with row = wm 64 + 32 i + l % 32 and col = wn 64 + 32 j + 8 g + 4 (l / 32).
+    // With VEC (N % 4 == 0) a 4-column group is wholly inside or outside C
+    // and C rows are 16-byte aligned when C is, which the caller checked.
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + 32 * j + l32;
+            const int row = m0 + wm * 64 + 32 * i + l32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M && col < N) {
-                    const size_t idx = static_cast<size_t>(row) * N + col;
-                    float out = alpha * acc[i][j][r];
-                    if (beta != 0.0f) out = fmaf(beta, C[idx], out);
-                    C[idx] = out;
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * h;
+                if (row >= M) continue;
+                float *c = C + static_cast<size_t>(row) * N + col;
+                if (VEC) {
+                    if (col >= N) continue;
+                    f32x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = alpha * acc[i][j][4 * g + e];
+                    if (beta != 0.0f) {
+                        const f32x4 cin = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                    }
+                    *reinterpret_cast<f32x4 *>(c) = out;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (col + e < N) {
+                            float out = alpha * acc[i][j][4 * g + e];
+                            if (beta != 0.0f) out = fmaf(beta, c[e], out);
+                            c[e] = out;
+                        }
+                    }
                 }
             }
         }

@@ -20,8 +20,8 @@ hipError_t launch_scale_c(int M, int N, float beta, float *C, hipStream_t stream
 // Fill `count` ints with zero (workspace counters).
 hipError_t launch_zero_ints(int *p, int count, hipStream_t stream);
 
-// fp32 LDS-tiled fp32-MFMA kernel.  `vec` selects 16-byte loads, which need
-// K % 4 == 0, N % 4 == 0 and 16-byte aligned A and B.
+// fp32 LDS-tiled fp32-MFMA kernel.  `vec` selects 16-byte accesses, which
+// need K % 4 == 0, N % 4 == 0 and 16-byte aligned A, B and C.
 hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const float *A,
                            const float *B, float *C, bool vec, hipStream_t stream);
 const char *f32_mfma_name(bool vec);
