@@ -184,6 +184,62 @@ __device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
     }
 }
 
+// Epilogue through LDS for a wave tile 64 columns wide: the wave writes 64
+// rows of its tile into a private 16 KB LDS region (16-byte chunk c of row r
+// at position c ^ (r % 16), so the 16 lanes served together hit 64 distinct
+// banks both when writing and when reading back), reads them back row by
+// row and stores them with 16 lanes per 256-byte row segment, four rows per
+// instruction: every store instruction covers 8 whole 128-byte lines instead
+// of 32 partial ones.  Same semantics and edge handling as store_c_tile.
+template <int MI, int NI>
+__device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], float *region,
+                                                 __amdgpu_buffer_rsrc_t rc, int row0, int col0,
+                                                 int cols_left, int N, float alpha, float beta) {
+    static_assert(NI * 32 == 64 && MI % 2 == 0, "wave tile must be (64 k) x 64");
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, h = lane >> 5;
+    const bool read_c = beta != 0.0f;
+#pragma unroll
+    for (int half = 0; half < MI / 2; ++half) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+            const int r = 32 * i2 + l32;
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int chunk = 8 * jj + 2 * g + h;
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[2 * half + i2][jj][4 * g + e];
+                    *reinterpret_cast<f32x4 *>(&region[r * 64 + ((chunk ^ (r & 15)) * 4)]) = v;
+                }
+        }
+        const int chunk = lane & 15;
+        const int col = col0 + 4 * chunk;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = 4 * j + (lane >> 4);
+            const f32x4 v =
+                *reinterpret_cast<const f32x4 *>(&region[r * 64 + ((chunk ^ (r & 15)) * 4)]);
+            const int row = row0 + 64 * half + r;
+            const uint32_t off =
+                col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+            f32x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
+            if (read_c) {
+                const f32x4 cin = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
+                                                   static_cast<int>(off), 0, 0);
+        }
+    }
+}
+
 template <int BM, int BN, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, int K, float alpha,
                                                                 float beta,
@@ -612,10 +668,22 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     for (; t < steps; ++t) k_step(t, std::false_type());
 
     // ---- epilogue
+    // ---- epilogue.  After the last barrier no wave reads the LDS stages and
+    // no copy is in flight (every wave drained its copies before it), so
+    // each wave stages its tile through a private 16 KB slice of them:
+    // waves 0-3 (which finish first) in the A stages, waves 4-7 in the B
+    // stages.
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
-    store_c_tile<T::MI, T::NI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta);
+    if constexpr (T::WN == 64 && S * T::A_STAGE * 2 >= 4 * 16384 && S * T::B_STAGE * 2 >= 4 * 16384) {
+        float *region = wave < 4 ? reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096
+                                 : reinterpret_cast<float *>(&lds_b[0][0]) + (wave - 4) * 4096;
+        store_c_tile_lds<T::MI, T::NI>(acc, region, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha,
+                                       beta);
+    } else {
+        store_c_tile<T::MI, T::NI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta);
+    }
 }
 
 const Bf16TileConfig kConfigs[] = {
