@@ -7,6 +7,19 @@
 //     and running MFMAs (ping-pong), so MFMAs do not wait on LDS reads.
 // The tile picker at the end chooses between them by shape.
 //
+// Last-round split (ping-pong kernel).  A 256 x 256 tile count that leaves a
+// last round at most half full (2048 x 4096: 128 tiles; 2048 x 12288: 384 on
+// 256 CUs) wastes up to half of that round.  Its r tiles are then computed
+// by 2 r workgroups, each over half of the K steps: the lower-numbered one
+// of a pair posts its fp32 partial tile to an uncached workspace and raises
+// a flag (an epoch number chosen by the host per call); the higher-numbered
+// one waits for the flag and writes alpha * (own + partial) + beta * C.  Only
+// the higher-numbered workgroup waits and workgroups are dispatched in
+// increasing id order, so the wait always ends; the sum of two partials does
+// not depend on the order in which they are added.  The pages do not cover
+// this; it is the split-K idea applied to the wave-quantisation loss they
+// discuss for small grids.
+//
 // Structure of the four-wave kernel (page "Naive GEMM and Roofline
 // analysis", section 10.4, the three tile levels plus double buffering):
 //   * workgroup tile BM x BN (256 or 128 each), K step 64, 256 threads = four
@@ -191,10 +204,19 @@ __device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
 // row and stores them with 16 lanes per 256-byte row segment, four rows per
 // instruction: every store instruction covers 8 whole 128-byte lines instead
 // of 32 partial ones.  Same semantics and edge handling as store_c_tile.
-template <int MI, int NI>
+// Modes: kStoreC writes alpha * acc (+ beta * C); kPostPartial writes the raw
+// accumulators to a BM x BN row-major partial tile `rw` (ldw floats per row)
+// and never touches C; kAddPartial writes alpha * (acc + partial) (+ beta *
+// C), reading the partial tile with system-scope loads (it was written by a
+// workgroup on another XCD).
+enum EpilogueMode { kStoreC, kPostPartial, kAddPartial };
+constexpr int kSystemScope = 1 | 16;  // buffer cache policy sc0 sc1: no stale L1 / L2 copy
+
+template <int MI, int NI, EpilogueMode MODE>
 __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], float *region,
                                                  __amdgpu_buffer_rsrc_t rc, int row0, int col0,
-                                                 int cols_left, int N, float alpha, float beta) {
+                                                 int cols_left, int N, float alpha, float beta,
+                                                 __amdgpu_buffer_rsrc_t rw, int ldw) {
     static_assert(NI * 32 == 64 && MI % 2 == 0, "wave tile must be (64 k) x 64");
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
@@ -223,11 +245,24 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
             const f32x4 v =
                 *reinterpret_cast<const f32x4 *>(&region[r * 64 + ((chunk ^ (r & 15)) * 4)]);
             const int row = row0 + 64 * half + r;
+            const int woff = ((row * ldw) + col0 + 4 * chunk) * 4;  // tile-local
+            if (MODE == kPostPartial) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw, woff, 0,
+                                                       0);
+                continue;
+            }
             const uint32_t off =
                 col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
             f32x4 out;
+            if (MODE == kAddPartial) {
+                const f32x4 p = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, kSystemScope));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
+                for (int e = 0; e < 4; ++e) out[e] = alpha * (v[e] + p[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
+            }
             if (read_c) {
                 const f32x4 cin = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
@@ -506,14 +541,31 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
                                                          float beta,
                                                          const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, float *C,
-                                                         int tiles_m, int tiles_n) {
+                                                         int tiles_m, int tiles_n,
+                                                         PPSplit split_plan) {
     using T = PPTile<BM, BN>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][T::A_STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][T::B_STAGE];
 
+    // Tile and K range of this workgroup.  Workgroups below split_from own a
+    // whole tile (XCD-aware order); the rest come in pairs that share one of
+    // the remaining tiles: the first takes the K steps below split_step and
+    // posts its partial sums, the second takes the rest and adds them.
+    const int bid = blockIdx.x;
+    int v, split = -1;
+    if (bid < split_plan.split_from) {
+        v = xcd_remap(bid, split_plan.split_from);
+    } else {
+        const int q = bid - split_plan.split_from;
+        v = split_plan.split_from + (q >> 1);
+        split = q & 1;
+    }
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
+    grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int total_steps = (K + kPPBK - 1) / kPPBK;
+    const int t_begin = split == 1 ? split_plan.split_step : 0;
+    const int t_end = split == 0 ? split_plan.split_step : total_steps;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -545,7 +597,7 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
         bool a_ok;
     };
     auto step_copy = [&](int t) {
-        const int k0 = t * kPPBK, stage = t % S;
+        const int k0 = (t_begin + t) * kPPBK, stage = t % S;
         StepCopy c;
         c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
                          (static_cast<long long>(M - m0) * K - k0) * 2);
@@ -608,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
-    const int steps = (K + kPPBK - 1) / kPPBK;
+    const int steps = t_end - t_begin;
     constexpr int kWaitSteady = wait_vm(T::COPIES * (S - 2));
     constexpr int kWaitAll = wait_vm(0);
     for (int t = 0; t < S - 1; ++t)
@@ -676,14 +728,52 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
-    if constexpr (T::WN == 64 && S * T::A_STAGE * 2 >= 4 * 16384 && S * T::B_STAGE * 2 >= 4 * 16384) {
-        float *region = wave < 4 ? reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096
-                                 : reinterpret_cast<float *>(&lds_b[0][0]) + (wave - 4) * 4096;
-        store_c_tile_lds<T::MI, T::NI>(acc, region, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha,
-                                       beta);
-    } else {
-        store_c_tile<T::MI, T::NI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta);
+    static_assert(T::WN == 64 && S * T::A_STAGE * 2 >= 4 * 16384 &&
+                      S * T::B_STAGE * 2 >= 4 * 16384,
+                  "the epilogue stages 16 KB per wave through the LDS stages");
+    float *region = wave < 4 ? reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096
+                             : reinterpret_cast<float *>(&lds_b[0][0]) + (wave - 4) * 4096;
+    const int row0 = wm * T::WM, col0 = wn * T::WN;
+    if (split < 0) {
+        store_c_tile_lds<T::MI, T::NI, kStoreC>(acc, region, rc, row0, col0, N - n0, N, alpha,
+                                                beta, rc, 0);
+        return;
     }
+    // A split tile: its partial lives in the workspace slot of the pair.
+    const int slot = v - split_plan.split_from;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BM * BN, BM * BN * 4);
+    int *flag = split_plan.flags + slot;
+    if (split == 0) {
+        store_c_tile_lds<T::MI, T::NI, kPostPartial>(acc, region, rc, row0, col0, N - n0, N,
+                                                     alpha, beta, rw, BN);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
+    }
+    // The second of the pair waits for the first's flag.  The first has a
+    // lower workgroup id, is dispatched no later and never waits, so the
+    // wait ends; a bounded poll turns anything else into NaN output.
+    __shared__ int s_ready;
+    if (tid == 0) {
+        int ready = 0;
+        for (int poll = 0; poll < (1 << 22); ++poll) {
+            if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                split_plan.epoch) {
+                ready = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        s_ready = ready;
+    }
+    __syncthreads();
+    const float a = s_ready ? alpha : __builtin_nanf("");
+    store_c_tile_lds<T::MI, T::NI, kAddPartial>(acc, region, rc, row0, col0, N - n0, N, a, beta,
+                                                rw, BN);
 }
 
 const Bf16TileConfig kConfigs[] = {
@@ -723,17 +813,29 @@ hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16
 
 template <int BM, int BN, int S>
 hipError_t launch_pp(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                     const uint16_t *B, float *C, hipStream_t stream) {
+                     const uint16_t *B, float *C, const PPSplit *split, hipStream_t stream) {
     const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long tiles = tiles_m * tiles_n;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(tiles)), block(512);
+    if (tiles > 0x3fffffffLL) return hipErrorInvalidValue;
+    PPSplit plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0};
+    if (split != nullptr) {
+        const int steps = (K + kPPBK - 1) / kPPBK;
+        if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
+            split->split_step >= steps ||
+            (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)))
+            return hipErrorInvalidValue;
+        plan = *split;
+    }
+    const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
+    const dim3 block(512);
     if (K % kPPBK == 0)
-        bf16_pp_kernel<BM, BN, S, false><<<grid, block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+        bf16_pp_kernel<BM, BN, S, false><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
+            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+            plan);
     else
-        bf16_pp_kernel<BM, BN, S, true><<<grid, block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+        bf16_pp_kernel<BM, BN, S, true><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
+            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+            plan);
     return hipGetLastError();
 }
 
@@ -743,8 +845,20 @@ int bf16_num_tile_configs() { return kNumConfigs; }
 
 const Bf16TileConfig &bf16_tile_config(int cfg) { return kConfigs[cfg]; }
 
-int bf16_pick_tile_config(int M, int N, int K, int num_cus) {
-    (void)K;
+int bf16_pp_config() { return 4; }
+
+int bf16_pp_split_tiles(int M, int N, int K, int num_cus) {
+    // Split the last round when it is at most half full and each half of K
+    // keeps at least four steps.
+    const long long tiles =
+        static_cast<long long>((M + kPPTile - 1) / kPPTile) * ((N + kPPTile - 1) / kPPTile);
+    const long long r = num_cus > 0 ? tiles % num_cus : 0;
+    const int steps = (K + kPPBK - 1) / kPPBK;
+    if (r == 0 || 2 * r > num_cus || steps < 8) return 0;
+    return static_cast<int>(r);
+}
+
+int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
     // Estimated time = rounds x (workgroups sharing a CU) x tile area /
     // efficiency, where a partial last round counts half plus its filled
     // fraction (a half-empty round runs faster per tile: less contention).
@@ -757,8 +871,12 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus) {
         const int occ = lds_per_cu / tile_lds_bytes(c);
         const long long slots = static_cast<long long>(num_cus) * occ;
         const long long full = wgs / slots, rem = wgs % slots;
-        const double rounds =
+        double rounds =
             static_cast<double>(full) + (rem ? 0.5 + 0.5 * static_cast<double>(rem) / slots : 0.0);
+        // a split last round: half the K steps on twice the CUs, plus the
+        // exchange of partial tiles
+        if (allow_split && c == bf16_pp_config() && bf16_pp_split_tiles(M, N, K, num_cus) > 0)
+            rounds = static_cast<double>(full) + 0.6;
         const double cost = rounds * occ * bm * bn / kTileEfficiency[c];
         if (c == 0 || cost < best_cost) {
             best = c;
@@ -769,13 +887,15 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus) {
 }
 
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
-                            const uint16_t *A, const uint16_t *B, float *C, hipStream_t stream) {
+                            const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
+                            hipStream_t stream) {
+    if (split != nullptr && cfg != bf16_pp_config()) return hipErrorInvalidValue;
     switch (cfg) {
         case 0: return launch_cfg<256, 256>(M, N, K, alpha, beta, A, B, C, stream);
         case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, stream);
         case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, stream);
         case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, stream);
-        case 4: return launch_pp<256, 256, 4>(M, N, K, alpha, beta, A, B, C, stream);
+        case 4: return launch_pp<kPPTile, kPPTile, 4>(M, N, K, alpha, beta, A, B, C, split, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,11 +37,13 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
 // 2. Grouped order: tiles are walked column by column inside bands of
 //    group_m tile-rows, so the workgroups resident at one time reuse a few
 //    A row-panels and B column-panels from L2.
-__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
-                                            int group_m, int &tm, int &tn) {
-    int v = bid;
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
     const int full = nwg - (nwg % kNumXcd);
-    if (bid < full) v = (bid % kNumXcd) * (full / kNumXcd) + bid / kNumXcd;
+    return bid < full ? (bid % kNumXcd) * (full / kNumXcd) + bid / kNumXcd : bid;
+}
+
+__device__ __forceinline__ void grouped_tile(int v, int tiles_m, int tiles_n, int group_m,
+                                             int &tm, int &tn) {
     const int group_size = group_m * tiles_n;
     const int g = v / group_size;
     const int first_m = g * group_m;
@@ -49,6 +51,11 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int t
     const int r = v - g * group_size;
     tm = first_m + r % rows;
     tn = r / rows;
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
+                                            int group_m, int &tm, int &tn) {
+    grouped_tile(xcd_remap(bid, nwg), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace mgemm

@@ -34,9 +34,27 @@ struct Bf16TileConfig {
 };
 int bf16_num_tile_configs();
 const Bf16TileConfig &bf16_tile_config(int cfg);
-int bf16_pick_tile_config(int M, int N, int K, int num_cus);
+// `allow_split`: the ping-pong kernel may split its last round (see PPSplit).
+int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split);
+
+// Split of the ping-pong kernel's trailing tiles over K.  When the tile count
+// leaves a last round at most half full, its r tiles are each computed by two
+// workgroups, one per half of the K steps: the first posts its partial sums,
+// the second adds them and writes C, so the last round takes about half as
+// long on twice as many CUs.
+constexpr int kPPTile = 256;  // the ping-pong kernel's square tile
+struct PPSplit {
+    int split_from;   // tiles at or past this position in the order are split
+    int split_step;   // first K step (of 32) of the second half
+    float *partials;  // one kPPTile^2 fp32 tile per split tile, uncached memory
+    int *flags;       // one int per split tile, uncached, never equal to epoch on entry
+    int epoch;        // a value the flags have not held before this launch
+};
+int bf16_pp_config();                                          // the ping-pong tile index
+int bf16_pp_split_tiles(int M, int N, int K, int num_cus);    // 0: no split
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
-                            const uint16_t *A, const uint16_t *B, float *C, hipStream_t stream);
+                            const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
+                            hipStream_t stream);
 
 // Skinny-M (M <= 16) bf16 kernel that streams B once from HBM.  Needs
 // K % 8 == 0, N % 8 == 0 and 16-byte aligned A, B and C.  With splits > 1 the

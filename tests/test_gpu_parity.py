@@ -248,10 +248,11 @@ TILE_NAMES = ["bf16_mfma_256x256x64", "bf16_mfma_256x128x64", "bf16_mfma_128x256
                                    (264, 392, 1024), (260, 136, 128), (136, 520, 192)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_every_bf16_tile(tile, shape, monkeypatch):
-    """Every tile configuration: 1, 2, 3, 6 (with a K tail) and 16 K tiles,
-    ragged M and N edges."""
+    """Every tile configuration, whole tiles only: 1, 2, 3, 6 (with a K tail)
+    and 16 K tiles, ragged M and N edges."""
     monkeypatch.setenv("MGEMM_BF16_TILE", tile)
     monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
+    monkeypatch.setenv("MGEMM_PP_SPLIT", "0")
     case = make_case(*shape, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=21)
     C, name = run(case)
     assert name == tile
@@ -271,6 +272,35 @@ def test_skinny_splits(splits, shape, monkeypatch):
     C, name = run(case)
     assert name.startswith("skinny_bf16")
     check_full(case, C)
+
+
+@pytest.mark.parametrize("shape", [(500, 712, 320), (512, 768, 328), (4352, 4096, 256),
+                                   (200, 4096, 4096), (520, 776, 328), (264, 392, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_pp_split_tail(shape, monkeypatch):
+    """The ping-pong kernel with its last round split over K (tile counts of
+    6, 6, 272, 16, 12 and 4 on 256 CUs): exact on integer inputs, for every split
+    tile, a K tail and a mix of whole and split tiles; twice in a row, so the
+    second call relies on fresh flag epochs."""
+    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
+    for rep in range(2):
+        case = make_case(*shape, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=50 + rep)
+        C, name = run(case)
+        assert name == "bf16_pp_256x256x32_splitk", name
+        Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=True)
+        assert np.array_equal(C.astype(np.float64), Cref), (shape, rep)
+
+
+def test_pp_split_off(monkeypatch):
+    """MGEMM_PP_SPLIT=0 keeps the whole-tile kernel on a shape that would split."""
+    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    monkeypatch.setenv("MGEMM_PP_SPLIT", "0")
+    case = make_case(500, 712, 320, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=52)
+    C, name = run(case)
+    assert name == "bf16_pp_256x256x32", name
+    Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=True)
+    assert np.array_equal(C.astype(np.float64), Cref)
 
 
 def test_skinny_workspace_reuse(monkeypatch):
