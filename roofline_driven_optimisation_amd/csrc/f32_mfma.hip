@@ -136,17 +136,28 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
     for (int t = 0; t < ktiles; ++t) {
         const int cur = t & 1;
         if (t + 1 < ktiles) load_tile((t + 1) * kBK);
+        // Fragments are double-buffered in registers: the reads of k-pair
+        // s + 1 are issued before the four MFMAs of pair s, so the LDS
+        // latency hides behind 256 cycles of matrix work (the scheduling
+        // barriers keep the compiler from sinking the reads back).
+        float fa[2][2], fb[2][2];
+        auto read_frags = [&](int s, int buf) {
+            const int kk = 2 * s + h;
+            fa[buf][0] = As[cur][wm * 64 + l32][kk];
+            fa[buf][1] = As[cur][wm * 64 + 32 + l32][kk];
+            fb[buf][0] = Bs[cur][kk][wn * 64 + l32];
+            fb[buf][1] = Bs[cur][kk][wn * 64 + 32 + l32];
+        };
+        read_frags(0, 0);
 #pragma unroll
         for (int s = 0; s < kBK / 2; ++s) {
-            const int kk = 2 * s + h;
-            const float a0 = As[cur][wm * 64 + l32][kk];
-            const float a1 = As[cur][wm * 64 + 32 + l32][kk];
-            const float b0 = Bs[cur][kk][wn * 64 + l32];
-            const float b1 = Bs[cur][kk][wn * 64 + 32 + l32];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[1][1], 0, 0, 0);
+            const int buf = s & 1;
+            if (s + 1 < kBK / 2) read_frags(s + 1, buf ^ 1);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], fa[buf][0], acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], fa[buf][0], acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], fa[buf][1], acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], fa[buf][1], acc[1][1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (t + 1 < ktiles) store_tile(cur ^ 1);
         __syncthreads();
