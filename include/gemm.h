@@ -26,13 +26,16 @@
  * accepted; fast vectorised kernels run when rows are 16-byte aligned, other
  * inputs go to slower kernels that load element by element.
  *
- * Workspace.  The decode-shaped (skinny-M) bf16 path splits K across
- * workgroups and needs a scratch area for partial sums.  The library
- * allocates it lazily (hipMalloc) on the first such call for a given
+ * Workspace.  Two bf16 paths split K across workgroups and exchange partial
+ * sums through a scratch area: the decode-shaped (skinny-M) kernel, and the
+ * large-M kernel when its last round of 256 x 256 tiles would be at most half
+ * full.  The library allocates the area lazily (64 MiB + 128 KiB of uncached
+ * device memory, hipExtMallocWithFlags) on the first such call for a given
  * (device, stream) pair and reuses it afterwards; it is never freed before
  * process exit.  Concurrent calls on different streams get different
  * workspaces; concurrent calls from several host threads on one stream must
  * be serialised by the caller, as the stream would serialise them anyway.
+ * The fp32 path never uses a workspace.
  *
  * Errors.  No call aborts or throws across the ABI.  Negative sizes, or a
  * NULL pointer for a matrix with a non-zero number of elements, return
