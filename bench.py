@@ -118,11 +118,25 @@ class Prepared:
         return binding.last_kernel()
 
 
+SETTLE_S = 0.1  # minimum untimed warm-up, seconds
+
+
 def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
-    """(wall seconds per step, event seconds per launch) over `steps` launches."""
+    """(wall seconds per step, event seconds per launch) over `steps` launches.
+
+    The untimed warm-up is `warmup` launches and at least SETTLE_S seconds of
+    them: right after the operands are staged the GPU has not reached the
+    clock it holds under sustained load (bf16 4096^3 measured 130 us per
+    launch after 20 launches, 118-119 us after 200 or more, as in a 6 s
+    steady-state loop)."""
     import torch
-    for i in range(warmup):
+    i = 0
+    t0 = time.perf_counter()
+    while i < warmup or time.perf_counter() - t0 < SETTLE_S:
         p.launch(i, naive)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -264,7 +278,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--secondary-steps", type=int, default=50)
     ap.add_argument("--only", default="", help="comma-separated workloads to time "
                     "(profiling runs); skips the CPU baseline")
@@ -359,7 +373,7 @@ def main():
         "data": "synthetic: A, B ~ normal(0, 1/64) rounded to bf16, seed 0",
         "config": {"workload": "bf16-input fp32-accumulate GEMM M=N=K=4096, alpha=1, beta=0, "
                                "row-major, C fp32", "kernel": kname,
-                   "rotated_operand_sets": head.sets},
+                   "rotated_operand_sets": head.sets, "warmup_min_s": SETTLE_S},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
