@@ -29,13 +29,18 @@
  * Workspace.  Two bf16 paths split K across workgroups and exchange partial
  * sums through a scratch area: the decode-shaped (skinny-M) kernel, and the
  * large-M kernel when its last round of 256 x 256 tiles would be at most half
- * full.  The library allocates the area lazily (64 MiB + 128 KiB of uncached
- * device memory, hipExtMallocWithFlags) on the first such call for a given
- * (device, stream) pair and reuses it afterwards; it is never freed before
- * process exit.  Concurrent calls on different streams get different
- * workspaces; concurrent calls from several host threads on one stream must
- * be serialised by the caller, as the stream would serialise them anyway.
- * The fp32 path never uses a workspace.
+ * full.  The library allocates the area lazily on the first such call for a
+ * given (device, stream) pair and reuses it afterwards; it is never freed
+ * before process exit.  It is 64 MiB + 128 KiB of uncached device memory
+ * (hipExtMallocWithFlags), plus, for the skinny kernel, 32 MiB of ordinary
+ * device memory (hipMalloc) whose eighth x is used only by workgroups on XCD
+ * x.  Before its first use of the latter on a device, the library runs a
+ * small probe grid on the caller's stream and waits for it, to check that the
+ * device places workgroup b on XCD b % 8; where it does not, the skinny
+ * kernel reduces through the uncached area alone.  Concurrent calls on
+ * different streams get different workspaces; concurrent calls from several
+ * host threads on one stream must be serialised by the caller, as the stream
+ * would serialise them anyway.  The fp32 path never uses a workspace.
  *
  * Errors.  No call aborts or throws across the ABI.  Negative sizes, or a
  * NULL pointer for a matrix with a non-zero number of elements, return

@@ -69,4 +69,26 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
                               const uint16_t *B, float *C, int splits, float *partials,
                               int *counters, int counter_ints, hipStream_t stream);
 
+// Split-K skinny kernel with most of its reduction kept inside XCDs.  On a
+// device that runs workgroup b on XCD b % 8 (probe_xcd_mapping checks this),
+// the first 8 * floor(col_blocks / 8) column blocks are placed so that all
+// splits of a block share one XCD and reduce through its L2, in ordinary
+// (cached) device memory: `xcd_base` is kXcdCount blocks of kSkinnyXcdBytes,
+// block x touched only by workgroups on XCD x, each holding
+// kSkinnyXcdCounterInts counters (zero on entry and left zero on exit) and
+// then the partial sums.  The remaining col_blocks % 8 column blocks reduce
+// through `partials` and `counters` as in launch_skinny_bf16.
+// skinny_xcd_local_fits says whether a shape may use this form.
+constexpr int kXcdCount = 8;
+constexpr size_t kSkinnyXcdBytes = size_t(4) << 20;
+constexpr int kSkinnyXcdCounterInts = 16384;
+bool skinny_xcd_local_fits(int M, int N, int K, int splits);
+hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
+                                  const uint16_t *A, const uint16_t *B, float *C, int splits,
+                                  float *partials, int *counters, int counter_ints,
+                                  char *xcd_base, int xcd_group, hipStream_t stream);
+// Runs a probe grid on `stream`, waits for it, and sets *ok when every
+// workgroup b ran on XCD b % kXcdCount.
+hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream);
+
 }  // namespace mgemm

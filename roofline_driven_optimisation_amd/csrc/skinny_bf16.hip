@@ -35,13 +35,28 @@
 // Cross-XCD visibility.  The eight XCDs of an MI355X have private L2 caches.
 // A device-scope fence makes a workgroup's stores visible to the others by
 // writing back and invalidating its whole L2, which measured 3-10x slower
-// than the streaming itself when every split workgroup does it.  The
-// workspace (partials and counters) is therefore allocated uncached
-// (hipDeviceMallocUncached): its loads and stores bypass the L2s and reach
-// memory directly.  A writer waits until its partial stores are acknowledged
-// (s_waitcnt 0) before the barrier and the counter increment, and the last
-// workgroup reads the partials only after its atomic has returned, so it
-// observes every partial without any L2 maintenance.
+// than the streaming itself when every split workgroup does it.  Two ways
+// round it:
+//   * uncached scratch (hipDeviceMallocUncached): partials and counters
+//     bypass the L2s and reach memory directly.  A writer waits until its
+//     partial stores are acknowledged (s_waitcnt 0) before the barrier and
+//     the counter increment, and the last workgroup reads the partials only
+//     after its atomic has returned, so it observes every partial without
+//     any L2 maintenance;
+//   * XCD-local placement: the hardware places workgroup b on XCD b % 8 (the
+//     library checks this once per device by reading the XCC_ID hardware
+//     register from a probe grid), so the splits of a column block can all
+//     be put on one XCD.  Their partials and counter live in ordinary cached
+//     memory that no other XCD touches; L2 is the point of coherence for
+//     every CU of the XCD, so the same store / wait / atomic / load sequence
+//     is correct, with each step an L2 round trip instead of a memory one.
+//     Vector L1 caches are write-through and no line of a block's partials
+//     is read before its last workgroup reads it, so no L1 holds a stale copy.
+// Which column blocks share an XCD also decides which HBM channels the XCD
+// streams from at once: runs of three adjacent blocks (768 bytes of each B
+// row) measured faster than one, two, four or all of an XCD's blocks.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -74,18 +89,65 @@ struct Stage {
     u32x4 a[kDepth];
 };
 
+// XCD_LOCAL selects the placement and scratch of the split-K reduction.
+// false: workgroup b is split b % splits of column block b / splits; the
+// partials of split s are the M x N matrix at partials + s M N and the counter
+// of block cb is at counters + cb * counter_stride, all in uncached memory.
+// true: with col_blocks = 8 q + r, the r trailing column blocks take the
+// first r * splits workgroups (rounded up to a multiple of 8 by idle ones) and
+// reduce as above.  Then workgroup b runs on XCD x = b % 8, and j = b / 8
+// (counted from the end of that first part) is split j % splits of the
+// (j / splits)-th of the q column blocks given to XCD x: runs of xcd_group
+// adjacent blocks, dealt to the XCDs in turn.  XCD x uses only the scratch
+// block at xcd_base + x * kSkinnyXcdBytes (counters first, then the partials
+// of its column blocks, 128 columns wide), so that part of the reduction
+// stays in one XCD's L2.  Every XCD gets the same number of workgroups.
+template <bool XCD_LOCAL>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, float alpha,
                                                           float beta,
                                                           const uint16_t *__restrict__ A,
                                                           const uint16_t *__restrict__ B,
                                                           float *C, int splits, int kblk_per_split,
                                                           float *partials, int *counters,
-                                                          int counter_stride) {
+                                                          int counter_stride, char *xcd_base,
+                                                          int xcd_group) {
     __shared__ f32x4 red[kWaves][8][64];
     __shared__ int s_last;
 
-    const int cb = blockIdx.x / splits;
-    const int sp = blockIdx.x - cb * splits;
+    int cb, sp, cb_local = 0;
+    bool local = false;  // uniform over the workgroup
+    if (XCD_LOCAL) {
+        const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
+        const int rest = col_blocks % kXcdCount;
+        const int rest_groups = (rest * splits + kXcdCount - 1) / kXcdCount * kXcdCount;
+        const int b = blockIdx.x;
+        if (b < rest_groups) {
+            if (b >= rest * splits) return;  // padding: exits before any barrier
+            cb = col_blocks - rest + b / splits;
+            sp = b % splits;
+        } else {
+            // rest_groups % 8 == 0, so b - rest_groups runs on XCD b % 8 too
+            const int x = b % kXcdCount, j = (b - rest_groups) / kXcdCount;
+            local = true;
+            cb_local = j / splits;
+            sp = j - cb_local * splits;
+            {
+                const int q = col_blocks / kXcdCount, g = xcd_group;
+                const int full = (q / g) * g;
+                if (cb_local < full)
+                    cb = (cb_local / g) * kXcdCount * g + x * g + cb_local % g;
+                else
+                    cb = full * kXcdCount + x * (q - full) + (cb_local - full);
+            }
+            char *blk = xcd_base + static_cast<size_t>(x) * kSkinnyXcdBytes;
+            counters = reinterpret_cast<int *>(blk);
+            counter_stride = kCounterLine;
+            partials = reinterpret_cast<float *>(blk + kSkinnyXcdCounterInts * sizeof(int));
+        }
+    } else {
+        cb = blockIdx.x / splits;
+        sp = blockIdx.x - cb * splits;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,9 +277,20 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
 
     // one counter per column block, each on its own 128-byte line when the
     // counter block has room (atomics on one line are serialised)
-    int *counter = counters + cb * counter_stride;
+    int *counter = counters + (local ? cb_local : cb) * counter_stride;
+    // partials of split s for this lane: part + s * split_stride
+    const float *part;
+    size_t split_stride;
+    if (local) {
+        split_stride = static_cast<size_t>(M) * kSkinnyCols;
+        part = partials + static_cast<size_t>(cb_local) * splits * split_stride +
+               static_cast<size_t>(m) * kSkinnyCols + 8 * (l & 15);
+    } else {
+        split_stride = static_cast<size_t>(M) * N;
+        part = partials + static_cast<size_t>(m) * N + nn;
+    }
     if (ok) {
-        f32x4 *p = reinterpret_cast<f32x4 *>(partials + (static_cast<size_t>(sp) * M + m) * N + nn);
+        f32x4 *p = reinterpret_cast<f32x4 *>(const_cast<float *>(part) + sp * split_stride);
         p[0] = f32x4{v[0], v[1], v[2], v[3]};
         p[1] = f32x4{v[4], v[5], v[6], v[7]};
     }
@@ -238,8 +311,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int s = min(sb + u, splits - 1);
-                const f32x4 *p = reinterpret_cast<const f32x4 *>(
-                    partials + (static_cast<size_t>(s) * M + m) * N + nn);
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(part + s * split_stride);
                 p0[u] = p[0];
                 p1[u] = p[1];
             }
@@ -305,8 +377,80 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int counter_stride = col_blocks * kCounterLine <= counter_ints ? kCounterLine : 1;
     if (real_splits > 1 && col_blocks > counter_ints) return hipErrorInvalidValue;
-    skinny_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
-        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters, counter_stride);
+    skinny_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
+        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters, counter_stride,
+        nullptr, 1);
+    return hipGetLastError();
+}
+
+namespace {
+
+// Fills xcc[b] with the XCD that workgroup b ran on (hardware register
+// XCC_ID, bits 3:0).
+__global__ __launch_bounds__(64) void xcd_probe_kernel(int *xcc, int count) {
+    const int id = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
+    if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < count) xcc[blockIdx.x] = id;
+}
+
+}  // namespace
+
+hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream) {
+    *ok = false;
+    constexpr int kProbeGroups = 4096;
+    int *d = nullptr;
+    hipError_t e = hipMalloc(&d, kProbeGroups * sizeof(int));
+    if (e != hipSuccess) return e;
+    static int h[kProbeGroups];
+    static std::mutex mu;
+    std::lock_guard<std::mutex> lock(mu);
+    xcd_probe_kernel<<<dim3(kProbeGroups), dim3(64), 0, stream>>>(d, kProbeGroups);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    (void)hipFree(d);
+    if (e != hipSuccess) return e;
+    bool all = true;
+    for (int b = 0; b < kProbeGroups; ++b) all = all && h[b] == b % kXcdCount;
+    *ok = all;
+    return hipSuccess;
+}
+
+bool skinny_xcd_local_fits(int M, int N, int K, int splits) {
+    const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
+    const int kblks = (K + kKBlock - 1) / kKBlock;
+    const int per = (kblks + splits - 1) / splits > 0 ? (kblks + splits - 1) / splits : 1;
+    const int real_splits = (kblks + per - 1) / per;
+    const int mine = col_blocks / kXcdCount;  // XCD-local column blocks per XCD
+    if (real_splits < 2 || M < 1 || M > kSkinnyMaxM || mine < 1) return false;
+    if (mine * kCounterLine > kSkinnyXcdCounterInts) return false;
+    return static_cast<long long>(mine) * real_splits * M * kSkinnyCols * sizeof(float) <=
+           static_cast<long long>(kSkinnyXcdBytes - kSkinnyXcdCounterInts * sizeof(int));
+}
+
+hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
+                                  const uint16_t *A, const uint16_t *B, float *C, int splits,
+                                  float *partials, int *counters, int counter_ints,
+                                  char *xcd_base, int xcd_group, hipStream_t stream) {
+    if (xcd_base == nullptr || !skinny_xcd_local_fits(M, N, K, splits)) return hipErrorInvalidValue;
+    const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
+    const int kblks = (K + kKBlock - 1) / kKBlock;
+    const int per = (kblks + splits - 1) / splits;
+    if (static_cast<long long>(per) * kKBlock * N * 2 >= 0x7fff0000LL ||
+        static_cast<long long>(M) * K * 2 >= 0x7fff0000LL)
+        return hipErrorInvalidValue;
+    const int real_splits = (kblks + per - 1) / per;
+    const int rest = col_blocks % kXcdCount;
+    if (rest > 0 && (partials == nullptr || counters == nullptr || col_blocks > counter_ints))
+        return hipErrorInvalidValue;
+    const int counter_stride = col_blocks * kCounterLine <= counter_ints ? kCounterLine : 1;
+    const long long rest_groups =
+        (static_cast<long long>(rest) * real_splits + kXcdCount - 1) / kXcdCount * kXcdCount;
+    const long long grid =
+        rest_groups + static_cast<long long>(col_blocks - rest) * real_splits;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    skinny_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
+        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters, counter_stride,
+        xcd_base, xcd_group < 1 ? 1 : xcd_group);
     return hipGetLastError();
 }
 

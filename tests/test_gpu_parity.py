@@ -263,14 +263,33 @@ def test_every_bf16_tile(tile, shape, monkeypatch):
     check_full(case, C)
 
 
+def xcd_local_expected(M, N, K, splits):
+    """Whether the split skinny kernel should take its XCD-local form: more
+    than one split after rounding and at least 8 column blocks of 128."""
+    kblks = -(-K // 32)
+    per = max(1, -(-kblks // splits))
+    real = -(-kblks // per)
+    return real > 1 and -(-N // 128) >= 8
+
+
+@pytest.mark.parametrize("xcd", ["1", "0"])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
-@pytest.mark.parametrize("shape", [(16, 4096, 11008), (1, 520, 4096), (5, 136, 264)],
+@pytest.mark.parametrize("shape", [(16, 4096, 11008), (1, 520, 4096), (5, 136, 264),
+                                   (7, 11008, 1024), (3, 1024, 4096), (2, 1160, 2048)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_skinny_splits(splits, shape, monkeypatch):
+def test_skinny_splits(splits, shape, xcd, monkeypatch):
+    """Split counts from 1 to 64 on both reductions: per-XCD L2 scratch
+    (column-block counts 32, 8, and 86 and 10, whose last 6 and 2 blocks
+    reduce through uncached scratch) and uncached scratch alone."""
     monkeypatch.setenv("MGEMM_SKINNY_SPLITS", str(splits))
+    monkeypatch.setenv("MGEMM_SKINNY_XCD", xcd)
     case = make_case(*shape, "bf16", 1.5, 0.5, "n:1", "n:0.02", seed=23)
     C, name = run(case)
     assert name.startswith("skinny_bf16")
+    if xcd == "1" and xcd_local_expected(*shape, splits):
+        assert name == "skinny_bf16_splitk_xcd", name
+    else:
+        assert name != "skinny_bf16_splitk_xcd", name
     check_full(case, C)
 
 
@@ -303,19 +322,46 @@ def test_pp_split_off(monkeypatch):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
-def test_skinny_workspace_reuse(monkeypatch):
+@pytest.mark.parametrize("group", [1, 2, 4, 5, 99])
+@pytest.mark.parametrize("shape", [(16, 11008, 4096), (1, 4096, 11008), (3, 1160, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_skinny_xcd_groups(group, shape, monkeypatch):
+    """Every way of dealing column blocks to XCDs (runs of 1, 2, 4, 5 or all
+    of an XCD's blocks; 10, 4 and 1 blocks per XCD) covers each block once:
+    exact on integer inputs."""
+    monkeypatch.setenv("MGEMM_SKINNY_XCD_GROUP", str(group))
+    case = make_case(*shape, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=26)
+    C, name = run(case)
+    assert name == "skinny_bf16_splitk_xcd", name
+    Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=True)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("mode", ["uncached", "xcd", "mixed"])
+def test_skinny_workspace_reuse(mode, monkeypatch):
     """Consecutive split-K calls on one stream with different shapes and split
-    counts share one workspace: each call must find every slot re-armed by the
-    call before it (exact match on integer inputs, every call)."""
-    plan = [((16, 4096, 2048), 8), ((1, 520, 4096), 3), ((16, 1032, 8192), 24),
-            ((7, 4096, 1024), 2), ((16, 4096, 2048), 8), ((1, 136, 512), 16),
-            ((16, 1032, 8192), 5)]
+    counts share one scratch area per reduction: each call must find every
+    counter re-armed by the call before it (exact match on integer inputs,
+    every call).  "mixed" alternates the two reductions call by call."""
+    plan = [((16, 4096, 2048), 8), ((1, 1024, 8192), 32), ((16, 11008, 4096), 4),
+            ((7, 4096, 1024), 2), ((16, 4096, 2048), 8), ((4, 11008, 4096), 8),
+            ((16, 2048, 4096), 3)]
+    if mode != "xcd":
+        plan += [((1, 520, 4096), 3), ((16, 896, 8192), 24), ((1, 136, 512), 16),
+                 ((16, 896, 8192), 5)]
+    else:
+        plan += [((16, 1032, 8192), 24), ((1, 1160, 4096), 7)]
     for rep in range(2):
         for i, (shape, splits) in enumerate(plan):
+            xcd = {"uncached": "0", "xcd": "1", "mixed": "01"[(i + rep) % 2]}[mode]
             monkeypatch.setenv("MGEMM_SKINNY_SPLITS", str(splits))
+            monkeypatch.setenv("MGEMM_SKINNY_XCD", xcd)
             case = make_case(*shape, "bf16", 1.0, 0.5, "i:4", "i:4", "i:4", seed=40 + i)
             C, name = run(case)
-            assert name == "skinny_bf16_splitk", (shape, splits, name)
+            local = xcd == "1" and xcd_local_expected(*shape, splits)
+            want = "skinny_bf16_splitk_xcd" if local else "skinny_bf16_splitk"
+            assert mode != "xcd" or local
+            assert name == want, (shape, splits, name)
             Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.0, 0.5, bf16=True)
             assert np.array_equal(C.astype(np.float64), Cref), (rep, shape, splits)
 
@@ -344,7 +390,8 @@ def test_side_stream(gpu):
 def test_dispatch_names():
     cases = [
         (make_case(256, 256, 256, "f32"), "f32_mfma_128x128x32_vec4"),
-        (make_case(16, 4096, 4096, "bf16"), "skinny_bf16_splitk"),
+        (make_case(16, 4096, 4096, "bf16"), "skinny_bf16_splitk_xcd"),
+        (make_case(16, 896, 4096, "bf16"), "skinny_bf16_splitk"),
         (make_case(4096, 4096, 64, "bf16"), None),
     ]
     for case, want in cases:
