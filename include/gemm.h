@@ -32,12 +32,12 @@
  * full.  The library allocates the area lazily on the first such call for a
  * given (device, stream) pair and reuses it afterwards; it is never freed
  * before process exit.  It is 64 MiB + 128 KiB of uncached device memory
- * (hipExtMallocWithFlags), plus, for the skinny kernel, 32 MiB of ordinary
- * device memory (hipMalloc) whose eighth x is used only by workgroups on XCD
- * x.  Before its first use of the latter on a device, the library runs a
+ * (hipExtMallocWithFlags), plus 96 MiB + 64 KiB of ordinary device memory
+ * (hipMalloc) through which workgroups that share an XCD exchange partial
+ * sums.  Before its first use of the latter on a device, the library runs a
  * small probe grid on the caller's stream and waits for it, to check that the
- * device places workgroup b on XCD b % 8; where it does not, the skinny
- * kernel reduces through the uncached area alone.  Concurrent calls on
+ * device places workgroup b on XCD b % 8; where it does not, both paths
+ * exchange through the uncached area alone.  Concurrent calls on
  * different streams get different workspaces; concurrent calls from several
  * host threads on one stream must be serialised by the caller, as the stream
  * would serialise them anyway.  The fp32 path never uses a workspace.

@@ -11,14 +11,17 @@
 // last round at most half full (2048 x 4096: 128 tiles; 2048 x 12288: 384 on
 // 256 CUs) wastes up to half of that round.  Its r tiles are then computed
 // by 2 r workgroups, each over half of the K steps: the lower-numbered one
-// of a pair posts its fp32 partial tile to an uncached workspace and raises
-// a flag (an epoch number chosen by the host per call); the higher-numbered
-// one waits for the flag and writes alpha * (own + partial) + beta * C.  Only
-// the higher-numbered workgroup waits and workgroups are dispatched in
-// increasing id order, so the wait always ends; the sum of two partials does
-// not depend on the order in which they are added.  The pages do not cover
-// this; it is the split-K idea applied to the wave-quantisation loss they
-// discuss for small grids.
+// of a pair posts its fp32 partial tile and raises a flag (an epoch number
+// chosen by the host per call); the higher-numbered one waits for the flag
+// and writes alpha * (own + partial) + beta * C.  Only the higher-numbered
+// workgroup waits and workgroups are dispatched in increasing id order, so
+// the wait always ends; the sum of two partials does not depend on the order
+// in which they are added.  When r is a multiple of 8 the pair is workgroups
+// b and b + 8, which the hardware places on the same XCD, and the partial
+// goes through that XCD's L2 in ordinary memory; otherwise the pair is 2i
+// and 2i + 1, on different XCDs, and the partial goes through uncached
+// memory.  The pages do not cover this; it is the split-K idea applied to
+// the wave-quantisation loss they discuss for small grids.
 //
 // Structure of the four-wave kernel (page "Naive GEMM and Roofline
 // analysis", section 10.4, the three tile levels plus double buffering):
@@ -207,12 +210,14 @@ __device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
 // Modes: kStoreC writes alpha * acc (+ beta * C); kPostPartial writes the raw
 // accumulators to a BM x BN row-major partial tile `rw` (ldw floats per row)
 // and never touches C; kAddPartial writes alpha * (acc + partial) (+ beta *
-// C), reading the partial tile with system-scope loads (it was written by a
-// workgroup on another XCD).
+// C).  PLOAD is the cache policy of the partial loads: system scope (sc0
+// sc1) when the partial was written on another XCD, device scope (sc1: past
+// the CU's L1, served by the XCD's L2) when it was written on the same XCD.
 enum EpilogueMode { kStoreC, kPostPartial, kAddPartial };
 constexpr int kSystemScope = 1 | 16;  // buffer cache policy sc0 sc1: no stale L1 / L2 copy
+constexpr int kDeviceScope = 16;      // buffer cache policy sc1: no stale L1 copy
 
-template <int MI, int NI, EpilogueMode MODE>
+template <int MI, int NI, EpilogueMode MODE, int PLOAD = kSystemScope>
 __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], float *region,
                                                  __amdgpu_buffer_rsrc_t rc, int row0, int col0,
                                                  int cols_left, int N, float alpha, float beta,
@@ -256,7 +261,7 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
             f32x4 out;
             if (MODE == kAddPartial) {
                 const f32x4 p = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, kSystemScope));
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, PLOAD));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) out[e] = alpha * (v[e] + p[e]);
             } else {
@@ -555,6 +560,13 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     int v, split = -1;
     if (bid < split_plan.split_from) {
         v = xcd_remap(bid, split_plan.split_from);
+    } else if (split_plan.xcd_pairs) {
+        // workgroups b and b + 8 share a tile, so both run on one XCD; the
+        // pairs of an XCD take consecutive tiles
+        const int q = bid - split_plan.split_from;
+        const int p = (q >> 4) * 8 + (q & 7);
+        v = split_plan.split_from + xcd_remap(p, (split_plan.grid_tiles - split_plan.split_from));
+        split = (q >> 3) & 1;
     } else {
         const int q = bid - split_plan.split_from;
         v = split_plan.split_from + (q >> 1);
@@ -744,14 +756,24 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BM * BN, BM * BN * 4);
     int *flag = split_plan.flags + slot;
+    // Uncached workspace (pairs on different XCDs): system-scope flag
+    // accesses reach memory.  XCD-local pairs use ordinary memory whose
+    // coherence point for both is their L2: the flag is stored with device
+    // scope and polled with device-scope loads, which skip the CU's L1.
+    const bool local = split_plan.xcd_pairs != 0;
     if (split == 0) {
         store_c_tile_lds<T::MI, T::NI, kPostPartial>(acc, region, rc, row0, col0, N - n0, N,
                                                      alpha, beta, rw, BN);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
         __syncthreads();
-        if (tid == 0)
-            __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_SYSTEM);
+        if (tid == 0) {
+            if (local)
+                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
         return;
     }
     // The second of the pair waits for the first's flag.  The first has a
@@ -761,8 +783,9 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     if (tid == 0) {
         int ready = 0;
         for (int poll = 0; poll < (1 << 22); ++poll) {
-            if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
-                split_plan.epoch) {
+            const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (f == split_plan.epoch) {
                 ready = 1;
                 break;
             }
@@ -772,8 +795,12 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     }
     __syncthreads();
     const float a = s_ready ? alpha : __builtin_nanf("");
-    store_c_tile_lds<T::MI, T::NI, kAddPartial>(acc, region, rc, row0, col0, N - n0, N, a, beta,
-                                                rw, BN);
+    if (local)
+        store_c_tile_lds<T::MI, T::NI, kAddPartial, kDeviceScope>(acc, region, rc, row0, col0,
+                                                                  N - n0, N, a, beta, rw, BN);
+    else
+        store_c_tile_lds<T::MI, T::NI, kAddPartial>(acc, region, rc, row0, col0, N - n0, N, a,
+                                                    beta, rw, BN);
 }
 
 const Bf16TileConfig kConfigs[] = {
@@ -817,14 +844,16 @@ hipError_t launch_pp(int M, int N, int K, float alpha, float beta, const uint16_
     const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x3fffffffLL) return hipErrorInvalidValue;
-    PPSplit plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0};
+    PPSplit plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
     if (split != nullptr) {
         const int steps = (K + kPPBK - 1) / kPPBK;
         if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
             split->split_step >= steps ||
-            (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)))
+            (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
+            (split->xcd_pairs && (tiles - split->split_from) % 8 != 0))
             return hipErrorInvalidValue;
         plan = *split;
+        plan.grid_tiles = static_cast<int>(tiles);
     }
     const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
     const dim3 block(512);

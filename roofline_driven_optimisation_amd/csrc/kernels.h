@@ -49,6 +49,13 @@ struct PPSplit {
     float *partials;  // one kPPTile^2 fp32 tile per split tile, uncached memory
     int *flags;       // one int per split tile, uncached, never equal to epoch on entry
     int epoch;        // a value the flags have not held before this launch
+    // 0: workgroups 2i and 2i + 1 share a tile (different XCDs); partials and
+    // flags must be uncached.  1: workgroups b and b + 8 share a tile, which
+    // puts both on one XCD on a device that runs workgroup b on XCD b % 8;
+    // partials and flags are ordinary device memory that no other XCD uses
+    // during the launch, and the number of split tiles is a multiple of 8.
+    int xcd_pairs;
+    int grid_tiles;   // set by the launcher: the tile count
 };
 int bf16_pp_config();                                          // the ping-pong tile index
 int bf16_pp_split_tiles(int M, int N, int K, int num_cus);    // 0: no split
@@ -64,7 +71,9 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
 // exit); both must live in uncached device memory (hipDeviceMallocUncached).
 constexpr int kSkinnyMaxM = 16;
 constexpr int kSkinnyCols = 128;  // output columns per workgroup
-int skinny_pick_splits(int M, int N, int K, int num_cus);
+// Split count for the decode shapes; `xcd_local` picks the rule for the
+// XCD-local reduction (launch_skinny_bf16_xcd), whose partials are cheaper.
+int skinny_pick_splits(int M, int N, int K, int num_cus, bool xcd_local);
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
                               int *counters, int counter_ints, hipStream_t stream);

@@ -330,23 +330,26 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
 
 }  // namespace
 
-int skinny_pick_splits(int M, int N, int K, int num_cus) {
+int skinny_pick_splits(int M, int N, int K, int num_cus, bool xcd_local) {
     // Measured on the decode shapes (4096 x 11008, 11008 x 4096, 4096 x
     // 32000, M = 1, 8, 16):
     //   * with about one 128-column block per CU already (the LM head: 250
     //     blocks) one split is best: every CU streams and no partials move
     //     (44.0 us against 47.4 us with eight splits);
-    //   * otherwise, at M <= 8, eight splits (688 or 256 workgroups);
-    //   * at M > 8 the partials are 16x larger, and the fewest splits that
-    //     reach every CU, rounded up to a power of two, win (22.6 us with
-    //     two splits against 24.0 us with eight at 16 x 4096 x 11008).
+    //   * otherwise, when the reduction stays in XCD-local L2, or at M <= 8,
+    //     eight splits (688 or 256 workgroups): 21.5 us against 22.0 us with
+    //     four at 16 x 4096 x 11008 with L2-local partials;
+    //   * through uncached memory at M > 8, where the partials are 16x
+    //     larger, the fewest splits that reach every CU, rounded up to a power
+    //     of two, win (22.6 us with two splits against 24.0 us with eight at
+    //     16 x 4096 x 11008).
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
     const int need = (num_cus + col_blocks - 1) / col_blocks;
     int splits;
     if (10 * col_blocks >= 9 * num_cus) {
         splits = 1;
-    } else if (M <= 8) {
+    } else if (M <= 8 || xcd_local) {
         splits = max(8, need);
     } else {
         splits = 2;
