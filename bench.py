@@ -163,6 +163,49 @@ def summary(p: Prepared, sec: float, kname: str) -> dict:
     }
 
 
+def launch_floor(per_graph: int = 200, replays: int = 10) -> dict:
+    """GPU-side cost of one launch: the library's smallest kernel (gemm_bf16
+    with K = 0 on a 1 x 8 C, i.e. C = 0 * C, one workgroup) captured
+    `per_graph` times into a graph, replayed and event-timed.  Host launch
+    overhead is excluded (from Python a direct call takes several times
+    longer than this), so it is what every launch costs the GPU itself, a
+    floor under any event-timed kernel of a few microseconds; the decode
+    entries report their HBM roofline fraction with and without it.  Each
+    replay is checked (C must read zero)."""
+    import torch
+    from roofline_driven_optimisation_amd import binding
+    A = torch.zeros(1, 0, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(0, 8, dtype=torch.bfloat16, device="cuda")
+    C = torch.ones(1, 8, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.gemm(A, B, C, 1.0, 0.0)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(per_graph):
+            binding.gemm(A, B, C, 1.0, 0.0)
+    kname = binding.last_kernel()
+    for _ in range(3):
+        C.fill_(1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        if not bool(torch.all(C == 0.0)):
+            raise RuntimeError("launch floor: graph replay gave a wrong C")
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / (replays * per_graph)
+    return {"us": round(us, 2), "kernel": kname,
+            "method": "graph of %d launches of C = 0*C (1x8, K = 0), %d replays, event-timed"
+                      % (per_graph, replays)}
+
+
 # Figures the pages quote, for context only (other machines; no MI355X number
 # exists in them, so vs_baseline stays null).
 PAGE_CONTEXT = {
@@ -349,6 +392,13 @@ def main():
         del p
         torch.cuda.empty_cache()
 
+    floor = launch_floor()
+    log("bench: launch floor " + json.dumps(floor))
+    for s_ in also:
+        if s_["bound"] == "hbm":
+            body = s_["us"] - floor["us"]
+            s_["frac_excl_launch_floor"] = round(s_["frac"] * s_["us"] / body, 4) if body > 0 else None
+
     ladder = None
     if not args.no_ladder:
         log("bench: naive rung, fp32 4092^3")
@@ -378,6 +428,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "also": also,
+        "launch_floor": floor,
         "ladder": ladder,
         "page_context": PAGE_CONTEXT,
     }

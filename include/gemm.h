@@ -36,11 +36,21 @@
  * (hipMalloc) through which workgroups that share an XCD exchange partial
  * sums.  Before its first use of the latter on a device, the library runs a
  * small probe grid on the caller's stream and waits for it, to check that the
- * device places workgroup b on XCD b % 8; where it does not, both paths
- * exchange through the uncached area alone.  Concurrent calls on
+ * device deals workgroups to its eight XCDs in round-robin order (ids equal
+ * modulo 8 share an XCD); where it does not, both paths exchange through the
+ * uncached area alone.  Concurrent calls on
  * different streams get different workspaces; concurrent calls from several
  * host threads on one stream must be serialised by the caller, as the stream
  * would serialise them anyway.  The fp32 path never uses a workspace.
+ *
+ * Graph capture.  A call on a stream that is being captured into a HIP graph
+ * allocates nothing, runs no probe and launches only kernels whose replays
+ * are independent: the decode-shaped kernel splits K only if the capturing
+ * stream already owns a workspace (from an earlier, uncaptured call on it;
+ * the kernel leaves its counters re-armed), and the large-M kernel never
+ * splits its last round (that split's flags are tagged with a per-call
+ * number that a replay would reuse).  Replays of such a graph use the
+ * capturing stream's workspace and must not overlap other calls on it.
  *
  * Errors.  No call aborts or throws across the ABI.  Negative sizes, or a
  * NULL pointer for a matrix with a non-zero number of elements, return

@@ -31,8 +31,9 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
 
 // Map a linear workgroup id to an output tile (tm, tn).
 //
-// 1. XCD-aware remap: workgroup b runs on XCD b % 8.  Consecutive "virtual"
-//    ids v are given to one XCD, so a run of neighbouring tiles shares that
+// 1. XCD-aware remap: workgroups are dealt to the eight XCDs in round-robin
+//    order, so ids equal modulo 8 share an XCD.  Consecutive "virtual"
+//    ids v are given to one such class, so a run of neighbouring tiles shares that
 //    XCD's L2 instead of being spread over all eight.
 // 2. Grouped order: tiles are walked column by column inside bands of
 //    group_m tile-rows, so the workgroups resident at one time reuse a few

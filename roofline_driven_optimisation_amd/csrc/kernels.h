@@ -51,7 +51,8 @@ struct PPSplit {
     int epoch;        // a value the flags have not held before this launch
     // 0: workgroups 2i and 2i + 1 share a tile (different XCDs); partials and
     // flags must be uncached.  1: workgroups b and b + 8 share a tile, which
-    // puts both on one XCD on a device that runs workgroup b on XCD b % 8;
+    // puts both on one XCD on a device that deals workgroups to its eight
+    // XCDs in round-robin order (probe_xcd_mapping checks this);
     // partials and flags are ordinary device memory that no other XCD uses
     // during the launch, and the number of split tiles is a multiple of 8.
     int xcd_pairs;
@@ -79,11 +80,12 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
                               int *counters, int counter_ints, hipStream_t stream);
 
 // Split-K skinny kernel with most of its reduction kept inside XCDs.  On a
-// device that runs workgroup b on XCD b % 8 (probe_xcd_mapping checks this),
+// device that deals workgroups to its eight XCDs in round-robin order, so
+// that ids equal modulo 8 share an XCD (probe_xcd_mapping checks this),
 // the first 8 * floor(col_blocks / 8) column blocks are placed so that all
 // splits of a block share one XCD and reduce through its L2, in ordinary
 // (cached) device memory: `xcd_base` is kXcdCount blocks of kSkinnyXcdBytes,
-// block x touched only by workgroups on XCD x, each holding
+// block x touched only by the workgroups with blockIdx % 8 == x, each holding
 // kSkinnyXcdCounterInts counters (zero on entry and left zero on exit) and
 // then the partial sums.  The remaining col_blocks % 8 column blocks reduce
 // through `partials` and `counters` as in launch_skinny_bf16.
@@ -97,7 +99,9 @@ hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
                                   float *partials, int *counters, int counter_ints,
                                   char *xcd_base, int xcd_group, hipStream_t stream);
 // Runs a probe grid on `stream`, waits for it, and sets *ok when every
-// workgroup b ran on XCD b % kXcdCount.
+// workgroups whose ids are equal modulo kXcdCount ran on one XCD and the
+// kXcdCount residues on different XCDs (which XCD takes workgroup 0 varies
+// between launches and is not checked).
 hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream);
 
 }  // namespace mgemm

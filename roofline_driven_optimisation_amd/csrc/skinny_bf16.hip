@@ -43,10 +43,12 @@
 //     the counter increment, and the last workgroup reads the partials only
 //     after its atomic has returned, so it observes every partial without
 //     any L2 maintenance;
-//   * XCD-local placement: the hardware places workgroup b on XCD b % 8 (the
-//     library checks this once per device by reading the XCC_ID hardware
-//     register from a probe grid), so the splits of a column block can all
-//     be put on one XCD.  Their partials and counter live in ordinary cached
+//   * XCD-local placement: the hardware deals workgroups to the eight XCDs
+//     in round-robin order, so workgroups whose ids are equal modulo 8 run on
+//     one XCD (which XCD takes workgroup 0 varies from launch to launch; the
+//     library checks the property once per device by reading the XCC_ID
+//     hardware register from a probe grid).  So the splits of a column block
+//     can all be put on one XCD.  Their partials and counter live in ordinary cached
 //     memory that no other XCD touches; L2 is the point of coherence for
 //     every CU of the XCD, so the same store / wait / atomic / load sequence
 //     is correct, with each step an L2 round trip instead of a memory one.
@@ -95,11 +97,12 @@ struct Stage {
 // of block cb is at counters + cb * counter_stride, all in uncached memory.
 // true: with col_blocks = 8 q + r, the r trailing column blocks take the
 // first r * splits workgroups (rounded up to a multiple of 8 by idle ones) and
-// reduce as above.  Then workgroup b runs on XCD x = b % 8, and j = b / 8
+// reduce as above.  Then the workgroups with b % 8 == x, which share one
+// XCD, form group x, and j = b / 8
 // (counted from the end of that first part) is split j % splits of the
 // (j / splits)-th of the q column blocks given to XCD x: runs of xcd_group
-// adjacent blocks, dealt to the XCDs in turn.  XCD x uses only the scratch
-// block at xcd_base + x * kSkinnyXcdBytes (counters first, then the partials
+// adjacent blocks, dealt to the groups in turn.  Group x uses only the
+// scratch block at xcd_base + x * kSkinnyXcdBytes (counters first, then the partials
 // of its column blocks, 128 columns wide), so that part of the reduction
 // stays in one XCD's L2.  Every XCD gets the same number of workgroups.
 template <bool XCD_LOCAL>
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
             cb = col_blocks - rest + b / splits;
             sp = b % splits;
         } else {
-            // rest_groups % 8 == 0, so b - rest_groups runs on XCD b % 8 too
+            // rest_groups % 8 == 0, so (b - rest_groups) % 8 == b % 8
             const int x = b % kXcdCount, j = (b - rest_groups) / kXcdCount;
             local = true;
             cb_local = j / splits;
@@ -389,10 +392,20 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
 namespace {
 
 // Fills xcc[b] with the XCD that workgroup b ran on (hardware register
-// XCC_ID, bits 3:0).
-__global__ __launch_bounds__(64) void xcd_probe_kernel(int *xcc, int count) {
+// XCC_ID, bits 3:0).  Its LDS footprint allows one workgroup per CU, so most
+// of the grid is dispatched late, as earlier workgroups retire (their busy
+// times differ, so they retire out of order).
+__global__ __launch_bounds__(256) void xcd_probe_kernel(int *xcc, int count) {
+    __shared__ float fill[36 * 1024];  // 144 KB
     const int id = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
-    if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < count) xcc[blockIdx.x] = id;
+    fill[threadIdx.x] = static_cast<float>(threadIdx.x);
+    const long long t0 = clock64();
+    const long long busy = 500LL * (1 + (blockIdx.x * 7919u) % 13);
+    while (clock64() - t0 < busy) {
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && static_cast<int>(blockIdx.x) < count)
+        xcc[blockIdx.x] = id + static_cast<int>(fill[1]) * 0;
 }
 
 }  // namespace
@@ -406,14 +419,23 @@ hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream) {
     static int h[kProbeGroups];
     static std::mutex mu;
     std::lock_guard<std::mutex> lock(mu);
-    xcd_probe_kernel<<<dim3(kProbeGroups), dim3(64), 0, stream>>>(d, kProbeGroups);
+    xcd_probe_kernel<<<dim3(kProbeGroups), dim3(256), 0, stream>>>(d, kProbeGroups);
     e = hipGetLastError();
     if (e == hipSuccess) e = hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     (void)hipFree(d);
     if (e != hipSuccess) return e;
+    // The XCD of workgroup 0 varies between launches (the dispatcher's
+    // round robin can carry over from earlier work); what the kernels rely
+    // on is that workgroups b and b' with b % 8 == b' % 8 share an XCD and
+    // that the eight residues cover eight different XCDs.
     bool all = true;
-    for (int b = 0; b < kProbeGroups; ++b) all = all && h[b] == b % kXcdCount;
+    unsigned seen = 0;
+    for (int b = 0; b < kXcdCount; ++b) {
+        all = all && h[b] >= 0 && h[b] < 32 && !(seen & (1u << h[b]));
+        if (h[b] >= 0 && h[b] < 32) seen |= 1u << h[b];
+    }
+    for (int b = kXcdCount; b < kProbeGroups; ++b) all = all && h[b] == h[b % kXcdCount];
     *ok = all;
     return hipSuccess;
 }

@@ -1,0 +1,84 @@
+"""The library under HIP graph capture (torch.cuda.graph).
+
+Under capture the library allocates nothing, runs no placement probe and
+never uses the ping-pong kernel's split tail (its flag epochs would be stale
+on replays).  A decode-shaped call uses split-K scratch only when the
+capturing stream already has it (the kernel leaves its counters re-armed, so
+every replay starts clean); otherwise it runs with one split.  Each graph is
+replayed several times with eager library work and synchronisations between
+the replays, and every replay is checked exactly against the oracle
+(integer inputs)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import to_device
+from roofline_driven_optimisation_amd import binding
+from roofline_driven_optimisation_amd.inputs import make_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.library()
+    oracle.build(force=False)
+    return torch
+
+
+def capture_and_check(torch, case, stream, warm, want_prefix, replays=4):
+    A, B, C = to_device(case)
+    C0 = C.clone()
+    ref, _ = oracle.gemm(case.A, case.B, case.C, case.alpha, case.beta, bf16=True)
+    if warm:  # a direct call on the capturing stream first: its scratch exists
+        with torch.cuda.stream(stream):
+            binding.gemm(A, B, C, case.alpha, case.beta)
+        stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        binding.gemm(A, B, C, case.alpha, case.beta)
+    name = binding.last_kernel()
+    assert name.startswith(want_prefix), name
+    # eager work between replays, on another shape through the same library
+    other = make_case(16, 1024, 512, "bf16", 1.0, 0.0, "i:4", "i:4", seed=81)
+    oA, oB, oC = to_device(other)
+    for r in range(replays):
+        C.copy_(C0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), (case.name, r)
+        binding.gemm(oA, oB, oC, 1.0, 0.0)
+        torch.cuda.synchronize()
+    return name
+
+
+@pytest.mark.parametrize("shape", [(16, 4096, 2048), (3, 1160, 2048), (1, 520, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_decode_split_scratch_existing(torch, shape):
+    """Scratch allocated by a direct call on the stream before capture."""
+    case = make_case(*shape, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=80)
+    s = torch.cuda.Stream()
+    name = capture_and_check(torch, case, s, warm=True, want_prefix="skinny_bf16_splitk")
+    print("  captured kernel", name, flush=True)
+
+
+def test_decode_fresh_stream_one_split(torch):
+    """No scratch on the capturing stream: one split, nothing allocated."""
+    case = make_case(16, 4096, 2048, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=82)
+    s = torch.cuda.Stream()
+    name = capture_and_check(torch, case, s, warm=False, want_prefix="skinny_bf16")
+    assert name == "skinny_bf16", name
+
+
+def test_pp_split_shape_unsplit_under_capture(torch, monkeypatch):
+    """A shape whose last round would be split runs whole tiles when captured."""
+    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
+    case = make_case(1024, 4096, 264, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=83)
+    s = torch.cuda.Stream()
+    name = capture_and_check(torch, case, s, warm=True, want_prefix="bf16_pp_256x256x32")
+    assert name == "bf16_pp_256x256x32", name
