@@ -1,7 +1,10 @@
 // bf16-input, fp32-accumulate GEMM on the gfx950 matrix cores
-// (v_mfma_f32_32x32x16_bf16), LDS-tiled and multi-buffered.  Two kernels:
+// (v_mfma_f32_32x32x16_bf16), LDS-tiled and multi-buffered.  Three kernels:
 //   * bf16_mfma_kernel: four waves, one per SIMD, K step 64, two LDS stages;
-//     each wave interleaves its LDS reads with its own MFMAs;
+//     each wave interleaves its LDS reads with its own MFMAs (the 256 x 128,
+//     128 x 256 and 128 x 128 tiles);
+//   * bf16_q4_kernel (further down): the 256 x 256 four-wave tile, K step
+//     32, four LDS stages filled three steps ahead;
 //   * bf16_pp_kernel (further down): eight waves, two per SIMD, K step 32,
 //     four LDS stages; the two waves of a SIMD take turns reading fragments
 //     and running MFMAs (ping-pong), so MFMAs do not wait on LDS reads.
@@ -803,8 +806,215 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
                                                     beta, rw, BN);
 }
 
+// ---------------------------------------------------------------------------
+// Four-wave 256 x 256 kernel on the ping-pong kernel's 32-k LDS layout:
+// 256 threads = four waves in 2 x 2, each owning a 128 x 128 wave tile (256
+// fp32 accumulators per lane, the whole AccVGPR file), K step 32, four LDS
+// stages (128 KB) filled by direct global -> LDS copies three K steps ahead.
+// Against the ping-pong kernel it reads a third less LDS per MFMA (128 x 128
+// wave tiles instead of 128 x 64), so at the board power limit it holds a
+// slightly higher clock, but a single wave per SIMD must hide its own LDS
+// reads and copies:
+//   * one K step = the last 8 MFMAs of the previous step's second k16
+//     sub-step (with this step's first fragment reads), the 16 MFMAs of
+//     sub-step 0 (with the reads of sub-step 1), the first 8 MFMAs of
+//     sub-step 1, a wait and a barrier.  An iteration ends at the barrier,
+//     where no LDS read is outstanding, so the compiler's wait counts inside
+//     the body are exact; reads are issued in the order the MFMAs use them;
+//   * the eight 1 KB copies of step t + 3 are spread over the step, one per
+//     four MFMAs in sub-step 0 and one per two after it.  Issuing them in a
+//     burst stalled the MFMA stream behind the copy queue (timing-only copies
+//     of the kernel: with L2-resident copies and no fragment reads it still
+//     took 40 % longer than with no copies at all);
+//   * the wait before the barrier leaves the copies of steps t + 2 and t + 3
+//     in flight and requires those of step t + 1 and every fragment read:
+//     the next stage is complete for every wave and the stage that step t +
+//     4's copies will overwrite is no longer read.
+// Edges: rows past M and B rows past K lie outside the copy descriptors
+// (zero-filled), columns past N are redirected out of range, A chunks past K
+// (a K tail) are skipped per step; the epilogue is store_c_tile.
+template <bool KTAIL>
+__global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, float alpha,
+                                                         float beta,
+                                                         const uint16_t *__restrict__ A,
+                                                         const uint16_t *__restrict__ B, float *C,
+                                                         int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256, S = 4, BK = kPPBK;
+    constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
+    constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
+    constexpr int A_LOADS = BM / 16 / 4;
+    constexpr int B_ROWS = 512 / BN;
+    constexpr int B_LOADS = BK / B_ROWS / 4;
+    constexpr int COPIES = A_LOADS + B_LOADS;
+    constexpr int B_CHUNKS = BN / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][A_STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][B_STAGE];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int a_row_in = lane >> 2;
+    const int a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t a_off = static_cast<uint32_t>(((16 * wave + a_row_in) * K + 8 * a_chunk) * 2);
+    const uint32_t a_step = static_cast<uint32_t>(64 * K * 2);
+    const int b_row0 = B_ROWS * wave + lane / B_CHUNKS;
+    const int b_c = (lane % B_CHUNKS) ^ swz_b(b_row0);
+    const bool b_ok = (n0 + 8 * b_c) < N;
+    const uint32_t b_off = static_cast<uint32_t>((b_row0 * N + 8 * b_c) * 2);
+    const uint32_t b_step = static_cast<uint32_t>(4 * B_ROWS * N * 2);
+
+    struct StepCopy {
+        i32x4 ra, rb;
+        uint32_t la, lb;
+        bool a_ok;
+    };
+    auto step_copy = [&](int t) {
+        const int k0 = t * BK, stage = t % S;
+        StepCopy c;
+        c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                         (static_cast<long long>(M - m0) * K - k0) * 2);
+        c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                         (static_cast<long long>(K - k0) * N - n0) * 2);
+        c.a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
+        c.la = lds_address(&lds_a[stage][wave * 512]);
+        c.lb = lds_address(&lds_b[stage][wave * 512]);
+        return c;
+    };
+    auto issue_copy = [&](const StepCopy &c, int q) {
+        if (q < A_LOADS)
+            lds_dma16(c.ra, c.la + q * 4 * 1024, c.a_ok ? a_off + q * a_step : kOOB);
+        else
+            lds_dma16(c.rb, c.lb + (q - A_LOADS) * 4 * 1024,
+                      b_ok ? b_off + (q - A_LOADS) * b_step : kOOB);
+    };
+
+    const int a_lane_base = (wm * WM + l32) * BK;
+    const int g = lane >> 4, j16 = lane & 15;
+    const int b_col_lane = wn * WN + 16 * (g & 1) + 4 * (j16 & 3);
+    const int b_row_lane = 8 * (g >> 1) + (j16 >> 2);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    constexpr int kReads = MI + 2 * NI;
+    auto read_one = [&](int stage, int s, int q, bf16x8 (&a)[MI], s16x8 (&b)[NI]) {
+        if (q < MI) {
+            const int pos = ((2 * s + h) ^ swz_a32(l32)) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                &lds_a[stage][a_lane_base + 32 * q * BK + pos]);
+            a[q] = __builtin_bit_cast(bf16x8, v);
+        } else {
+            const int jj = (q - MI) >> 1, r = (q - MI) & 1;
+            const int row = 16 * s + 4 * r + b_row_lane;
+            const int col = b_col_lane + 32 * jj;
+            const int chunk = (col >> 3) ^ swz_b(row);
+            const int elem = row * BN + chunk * 8 + (col & 7);
+            const s16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3))) *)&lds_b[stage][elem]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[jj][4 * r + e] = part[e];
+        }
+    };
+    // reads in consumption order: A block 0, all B blocks, the other A blocks
+    auto read_in_order = [&](int stage, int s, int r, bf16x8 (&a)[MI], s16x8 (&b)[NI]) {
+        const int q = r == 0 ? 0 : (r <= 2 * NI ? MI + r - 1 : r - 2 * NI);
+        read_one(stage, s, q, a, b);
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+    bf16x8 fa[2][MI];
+    s16x8 fb[2][NI];
+    auto mfma = [&](int q, int f) {
+        const int i = q / NI, jj = q % NI;
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, fb[f][jj]), fa[f][i], acc[i][jj], 0, 0, 0);
+    };
+    constexpr int kMfma = MI * NI;
+    constexpr int kEarly = 2 * NI;
+    constexpr int kTail = kMfma - kEarly;
+    // vmcnt <= vm and lgkmcnt == 0
+    constexpr int kWaitSteady = (2 * COPIES & 15) | (7 << 4) | ((2 * COPIES >> 4) << 14);
+    constexpr int kWaitDrain = (7 << 4);
+
+    const int T = (K + BK - 1) / BK;
+    for (int t = 0; t < S - 1; ++t)
+        if (t < T) {
+            const StepCopy c = step_copy(t);
+#pragma unroll
+            for (int q = 0; q < COPIES; ++q) issue_copy(c, q);
+        }
+    if (T >= S - 1)
+        __builtin_amdgcn_s_waitcnt(kWaitSteady);
+    else
+        __builtin_amdgcn_s_waitcnt(kWaitDrain);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kReads; ++r) read_in_order(0, 0, r, fa[0], fb[0]);
+
+    // One K step (stage t % 4): the tail of the previous step's second k16
+    // sub-step with this step's first reads; sub-step 0 with the reads of
+    // sub-step 1 and the copies of step t + 3; the first MFMAs of sub-step
+    // 1; wait for this wave's copies of step t + 1 (and all its reads);
+    // barrier.
+    auto k_step = [&](int t, auto copy_tag) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        const int cur = t % S;
+        if (t > 0) {
+#pragma unroll
+            for (int q = 0; q < kTail; ++q) {
+                mfma(kEarly + q, 1);
+                constexpr int per = (kReads + kTail - 1) / kTail;
+#pragma unroll
+                for (int u = 0; u < per; ++u)
+                    if (q * per + u < kReads) read_in_order(cur, 0, q * per + u, fa[0], fb[0]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        StepCopy next;
+        if (COPY) next = step_copy(t + S - 1);
+#pragma unroll
+        for (int q = 0; q < kMfma; ++q) {
+            mfma(q, 0);
+            if (q < kReads) read_in_order(cur, 1, q, fa[1], fb[1]);
+            if (COPY && (q & 3) == 0) issue_copy(next, q / 4);  // copies 0..3
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < kEarly; ++q) {
+            mfma(q, 1);
+            if (COPY && (q & 1) == 0) issue_copy(next, 4 + q / 2);  // copies 4..7
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(COPY ? kWaitSteady : kWaitDrain);
+        __syncthreads();
+    };
+    const int copy_end = max(0, T - (S - 1));
+    int t = 0;
+    for (; t < copy_end; ++t) k_step(t, std::true_type());
+    for (; t < T; ++t) k_step(t, std::false_type());
+#pragma unroll
+    for (int q = 0; q < kTail; ++q) {
+        mfma(kEarly + q, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + static_cast<size_t>(m0) * N + n0,
+                  (static_cast<long long>(M - m0) * N - n0) * 4);
+    store_c_tile<MI, NI>(acc, rc, wm * WM, wn * WN, N - n0, N, alpha, beta);
+}
+
+
 const Bf16TileConfig kConfigs[] = {
-    {256, 256, "bf16_mfma_256x256x64"},
+    {256, 256, "bf16_q4_256x256x32"},
     {256, 128, "bf16_mfma_256x128x64"},
     {128, 256, "bf16_mfma_128x256x64"},
     {128, 128, "bf16_mfma_128x128x64"},
@@ -813,13 +1023,33 @@ const Bf16TileConfig kConfigs[] = {
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 // Relative per-CU speed of each tile configuration at equal occupancy,
-// measured on the square and prefill shapes (the ping-pong kernel fastest,
-// the single-wave 256-wide tiles next; the 128 x 128 tile is the unit).
-const double kTileEfficiency[kNumConfigs] = {1.2, 0.85, 0.85, 1.0, 1.27};
+// measured on the square and prefill shapes (the 128 x 128 tile is the
+// unit).  At 4096^3 the four-wave 256 x 256 kernel ran 0.5-2.7 us ahead of
+// the ping-pong kernel on three boards out of four; a shape that leaves a
+// last round at most half full still goes to the ping-pong kernel, whose
+// split of that round (costed in the picker) is worth more.
+const double kTileEfficiency[kNumConfigs] = {1.29, 0.85, 0.85, 1.0, 1.27};
 // LDS bytes per workgroup, which set how many workgroups share a CU.
 int tile_lds_bytes(int c) {
     const Bf16TileConfig &t = kConfigs[c];
-    return c == 4 ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
+    return (c == 0 || c == 4) ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
+}
+
+hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_t *A,
+                     const uint16_t *B, float *C, hipStream_t stream) {
+    const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    if (K % kPPBK == 0)
+        bf16_q4_kernel<false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                          static_cast<int>(tiles_m),
+                                                          static_cast<int>(tiles_n));
+    else
+        bf16_q4_kernel<true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                         static_cast<int>(tiles_m),
+                                                         static_cast<int>(tiles_n));
+    return hipGetLastError();
 }
 
 template <int BM, int BN>
@@ -920,7 +1150,7 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
                             hipStream_t stream) {
     if (split != nullptr && cfg != bf16_pp_config()) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return launch_cfg<256, 256>(M, N, K, alpha, beta, A, B, C, stream);
+        case 0: return launch_q4(M, N, K, alpha, beta, A, B, C, stream);
         case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, stream);
         case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, stream);
         case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, stream);

@@ -18,6 +18,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import re
 import os
 import statistics
 from collections import defaultdict
@@ -27,18 +28,30 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "bf16_mfma": "bf16_mfma.hip",
     "bf16_pp": "bf16_mfma.hip",
+    "bf16_q4": "bf16_mfma.hip",
     "f32_mfma": "f32_mfma.hip",
     "skinny": "skinny_bf16.hip",
     "naive": "naive.hip",
 }
 
 
+def code_hash(text: str) -> str:
+    """sha256[:16] of C++/HIP source with comments, trailing blanks and empty
+    lines removed, so that editing a comment does not mark a measurement of
+    the code as stale.  (The sources hold no string literal containing
+    comment markers.)"""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+    code = "\n".join(line for line in lines if line)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def source_hash(kernel_family: str) -> str:
-    """sha256[:16] of the source that defines a kernel family."""
+    """code_hash of the source that defines a kernel family."""
     for prefix, fname in KERNEL_SOURCES.items():
         if kernel_family.startswith(prefix):
-            with open(os.path.join(HERE, "csrc", fname), "rb") as f:
-                return hashlib.sha256(f.read()).hexdigest()[:16]
+            with open(os.path.join(HERE, "csrc", fname)) as f:
+                return code_hash(f.read())
     return ""
 
 

@@ -239,7 +239,7 @@ def test_deterministic_repeat(gpu):
             assert torch.equal(o, outs[0]), name
 
 
-TILE_NAMES = ["bf16_mfma_256x256x64", "bf16_mfma_256x128x64", "bf16_mfma_128x256x64",
+TILE_NAMES = ["bf16_q4_256x256x32", "bf16_mfma_256x128x64", "bf16_mfma_128x256x64",
               "bf16_mfma_128x128x64", "bf16_pp_256x256x32"]
 
 
@@ -425,4 +425,4 @@ def test_dispatch_names():
         if want:
             assert name == want
         else:
-            assert name.startswith(("bf16_mfma_", "bf16_pp_"))
+            assert name.startswith(("bf16_mfma_", "bf16_pp_", "bf16_q4_"))
