@@ -865,9 +865,8 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
 // fp32 accumulators per lane, the whole AccVGPR file), K step 32, four LDS
 // stages (128 KB) filled by direct global -> LDS copies three K steps ahead.
 // Against the ping-pong kernel it reads a third less LDS per MFMA (128 x 128
-// wave tiles instead of 128 x 64), so at the board power limit it holds a
-// slightly higher clock, but a single wave per SIMD must hide its own LDS
-// reads and copies:
+// wave tiles instead of 128 x 64), but a single wave per SIMD must hide its
+// own LDS reads and copies:
 //   * one K step = the last 8 MFMAs of the previous step's second k16
 //     sub-step (with this step's first fragment reads), the 16 MFMAs of
 //     sub-step 0 (with the reads of sub-step 1), the first 8 MFMAs of
