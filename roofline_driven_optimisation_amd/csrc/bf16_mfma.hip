@@ -290,12 +290,14 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
 // when writing and when reading back), reads them back two rows per
 // instruction and stores them with 32 lanes per 512-byte row segment: each
 // store instruction covers 8 whole 128-byte lines.  C = alpha * acc (+ beta
-// * C); same edge handling as store_c_tile.
-template <int MI>
+// * C); same edge handling as store_c_tile.  MODE and PLOAD as for
+// store_c_tile_lds (a partial tile `rw` of ldw floats per row).
+template <int MI, EpilogueMode MODE = kStoreC, int PLOAD = kSystemScope>
 __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], float *region,
                                                     __amdgpu_buffer_rsrc_t rc, int row0,
                                                     int col0, int cols_left, int N, float alpha,
-                                                    float beta) {
+                                                    float beta, __amdgpu_buffer_rsrc_t rw,
+                                                    int ldw) {
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
     const bool read_c = beta != 0.0f;
@@ -319,11 +321,24 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
             const f32x4 v =
                 *reinterpret_cast<const f32x4 *>(&region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
             const int row = row0 + 32 * i + r;
+            const int woff = (row * ldw + col) * 4;  // tile-local
+            if (MODE == kPostPartial) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw, woff, 0,
+                                                       0);
+                continue;
+            }
             const uint32_t off =
                 col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
             f32x4 out;
+            if (MODE == kAddPartial) {
+                const f32x4 pp = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, PLOAD));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
+                for (int e = 0; e < 4; ++e) out[e] = alpha * (v[e] + pp[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
+            }
             if (read_c) {
                 const f32x4 cin = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
@@ -892,7 +907,8 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
                                                          float beta,
                                                          const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, float *C,
-                                                         int tiles_m, int tiles_n) {
+                                                         int tiles_m, int tiles_n,
+                                                         PPSplit split_plan) {
     constexpr int BM = 256, BN = 256, S = 4, BK = kPPBK;
     constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
@@ -904,9 +920,29 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][A_STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][B_STAGE];
 
+    // Tile and K range: as in the ping-pong kernel, workgroups below
+    // split_from own a whole tile (XCD-aware order) and the rest come in
+    // pairs that share a tile, one per half of the K steps.
+    const int bid = blockIdx.x;
+    int v, split = -1;
+    if (bid < split_plan.split_from) {
+        v = xcd_remap(bid, split_plan.split_from);
+    } else if (split_plan.xcd_pairs) {
+        const int q = bid - split_plan.split_from;
+        const int p = (q >> 4) * 8 + (q & 7);
+        v = split_plan.split_from + xcd_remap(p, (split_plan.grid_tiles - split_plan.split_from));
+        split = (q >> 3) & 1;
+    } else {
+        const int q = bid - split_plan.split_from;
+        v = split_plan.split_from + (q >> 1);
+        split = q & 1;
+    }
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
+    grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int total_steps = (K + BK - 1) / BK;
+    const int t_begin = split == 1 ? split_plan.split_step : 0;
+    const int t_end = split == 0 ? split_plan.split_step : total_steps;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -927,8 +963,8 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
         uint32_t la, lb;
         bool a_ok;
     };
-    auto step_copy = [&](int t) {
-        const int k0 = t * BK, stage = t % S;
+    auto step_copy = [&](int t) {  // t counts this workgroup's steps
+        const int k0 = (t_begin + t) * BK, stage = t % S;
         StepCopy c;
         c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
                          (static_cast<long long>(M - m0) * K - k0) * 2);
@@ -998,7 +1034,7 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     constexpr int kWaitSteady = (2 * COPIES & 15) | (7 << 4) | ((2 * COPIES >> 4) << 14);
     constexpr int kWaitDrain = (7 << 4);
 
-    const int T = (K + BK - 1) / BK;
+    const int T = t_end - t_begin;
     for (int t = 0; t < S - 1; ++t)
         if (t < T) {
             const StepCopy c = step_copy(t);
@@ -1068,7 +1104,56 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
                   (static_cast<long long>(M - m0) * N - n0) * 4);
     static_assert(S * A_STAGE * 2 >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
-    store_c_tile_lds128<MI>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta);
+    const int row0 = wm * WM, col0 = wn * WN;
+    if (split < 0) {
+        store_c_tile_lds128<MI>(acc, region, rc, row0, col0, N - n0, N, alpha, beta, rc, 0);
+        return;
+    }
+    // A split tile: the partial lives in the workspace slot of the pair; the
+    // handshake is the ping-pong kernel's (device-scope flag accesses for
+    // pairs on one XCD, system scope through uncached memory otherwise).
+    const int slot = v - split_plan.split_from;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BM * BN, BM * BN * 4);
+    int *flag = split_plan.flags + slot;
+    const bool local = split_plan.xcd_pairs != 0;
+    if (split == 0) {
+        store_c_tile_lds128<MI, kPostPartial>(acc, region, rc, row0, col0, N - n0, N, alpha,
+                                              beta, rw, BN);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+        __syncthreads();
+        if (tid == 0) {
+            if (local)
+                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        return;
+    }
+    __shared__ int s_ready;
+    if (tid == 0) {
+        int ready = 0;
+        for (int poll = 0; poll < (1 << 22); ++poll) {
+            const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (f == split_plan.epoch) {
+                ready = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        s_ready = ready;
+    }
+    __syncthreads();
+    const float a = s_ready ? alpha : __builtin_nanf("");
+    if (local)
+        store_c_tile_lds128<MI, kAddPartial, kDeviceScope>(acc, region, rc, row0, col0, N - n0,
+                                                           N, a, beta, rw, BN);
+    else
+        store_c_tile_lds128<MI, kAddPartial>(acc, region, rc, row0, col0, N - n0, N, a, beta,
+                                             rw, BN);
 }
 
 
@@ -1095,19 +1180,31 @@ int tile_lds_bytes(int c) {
 }
 
 hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                     const uint16_t *B, float *C, hipStream_t stream) {
+                     const uint16_t *B, float *C, const PPSplit *split, hipStream_t stream) {
     const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const long long tiles = tiles_m * tiles_n;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    if (tiles > 0x3fffffffLL) return hipErrorInvalidValue;
+    PPSplit plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
+    if (split != nullptr) {
+        const int steps = (K + kPPBK - 1) / kPPBK;
+        if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
+            split->split_step >= steps ||
+            (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
+            (split->xcd_pairs && (tiles - split->split_from) % 8 != 0))
+            return hipErrorInvalidValue;
+        plan = *split;
+        plan.grid_tiles = static_cast<int>(tiles);
+    }
+    const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
+    const dim3 block(kThreads);
     if (K % kPPBK == 0)
-        bf16_q4_kernel<false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                          static_cast<int>(tiles_m),
-                                                          static_cast<int>(tiles_n));
+        bf16_q4_kernel<false><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
+            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+            plan);
     else
-        bf16_q4_kernel<true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                         static_cast<int>(tiles_m),
-                                                         static_cast<int>(tiles_n));
+        bf16_q4_kernel<true><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
+            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+            plan);
     return hipGetLastError();
 }
 
@@ -1165,6 +1262,8 @@ const Bf16TileConfig &bf16_tile_config(int cfg) { return kConfigs[cfg]; }
 
 int bf16_pp_config() { return 4; }
 
+bool bf16_config_splits(int cfg) { return cfg == 0 || cfg == 4; }
+
 int bf16_pp_split_tiles(int M, int N, int K, int num_cus) {
     // Split the last round when it is at most half full and each half of K
     // keeps at least four steps.
@@ -1193,6 +1292,9 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
             static_cast<double>(full) + (rem ? 0.5 + 0.5 * static_cast<double>(rem) / slots : 0.0);
         // a split last round: half the K steps on twice the CUs, plus the
         // exchange of partial tiles
+        // (the four-wave kernel can split too, but measured no better on the
+        // prefill shapes and 8 % slower where every tile splits at K = 4096,
+        // so it is costed unsplit)
         if (allow_split && c == bf16_pp_config() && bf16_pp_split_tiles(M, N, K, num_cus) > 0)
             rounds = static_cast<double>(full) + 0.6;
         const double cost = rounds * occ * bm * bn / kTileEfficiency[c];
@@ -1207,9 +1309,9 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
                             hipStream_t stream) {
-    if (split != nullptr && cfg != bf16_pp_config()) return hipErrorInvalidValue;
+    if (split != nullptr && !bf16_config_splits(cfg)) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return launch_q4(M, N, K, alpha, beta, A, B, C, stream);
+        case 0: return launch_q4(M, N, K, alpha, beta, A, B, C, split, stream);
         case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, stream);
         case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, stream);
         case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, stream);

@@ -34,15 +34,16 @@ struct Bf16TileConfig {
 };
 int bf16_num_tile_configs();
 const Bf16TileConfig &bf16_tile_config(int cfg);
-// `allow_split`: the ping-pong kernel may split its last round (see PPSplit).
+// `allow_split`: a 256 x 256 kernel may split its last round (see PPSplit).
 int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split);
 
-// Split of the ping-pong kernel's trailing tiles over K.  When the tile count
+// Split of a 256 x 256 kernel's trailing tiles over K (the four-wave and the
+// ping-pong kernel share the scheme and the layout of the partials).  When the tile count
 // leaves a last round at most half full, its r tiles are each computed by two
 // workgroups, one per half of the K steps: the first posts its partial sums,
 // the second adds them and writes C, so the last round takes about half as
 // long on twice as many CUs.
-constexpr int kPPTile = 256;  // the ping-pong kernel's square tile
+constexpr int kPPTile = 256;  // the square tile of both 256 x 256 kernels
 struct PPSplit {
     int split_from;   // tiles at or past this position in the order are split
     int split_step;   // first K step (of 32) of the second half
@@ -59,6 +60,7 @@ struct PPSplit {
     int grid_tiles;   // set by the launcher: the tile count
 };
 int bf16_pp_config();                                          // the ping-pong tile index
+bool bf16_config_splits(int cfg);  // the 256 x 256 kernels, which can split a last round
 int bf16_pp_split_tiles(int M, int N, int K, int num_cus);    // 0: no split
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,

@@ -74,11 +74,12 @@ def test_decode_fresh_stream_one_split(torch):
     assert name == "skinny_bf16", name
 
 
-def test_pp_split_shape_unsplit_under_capture(torch, monkeypatch):
+@pytest.mark.parametrize("tile", ["bf16_pp_256x256x32", "bf16_q4_256x256x32"])
+def test_pp_split_shape_unsplit_under_capture(torch, tile, monkeypatch):
     """A shape whose last round would be split runs whole tiles when captured."""
-    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    monkeypatch.setenv("MGEMM_BF16_TILE", tile)
     monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
     case = make_case(1024, 4096, 264, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=83)
     s = torch.cuda.Stream()
-    name = capture_and_check(torch, case, s, warm=True, want_prefix="bf16_pp_256x256x32")
-    assert name == "bf16_pp_256x256x32", name
+    name = capture_and_check(torch, case, s, warm=True, want_prefix=tile)
+    assert name == tile, name

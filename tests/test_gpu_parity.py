@@ -293,24 +293,28 @@ def test_skinny_splits(splits, shape, xcd, monkeypatch):
     check_full(case, C)
 
 
+SPLIT_TILES = ["bf16_pp_256x256x32", "bf16_q4_256x256x32"]
+
+
+@pytest.mark.parametrize("tile", SPLIT_TILES)
 @pytest.mark.parametrize("xcd", ["1", "0"])
 @pytest.mark.parametrize("shape", [(500, 712, 320), (512, 768, 328), (4352, 4096, 256),
                                    (200, 4096, 4096), (520, 776, 328), (264, 392, 1024),
                                    (512, 2048, 328), (1024, 4096, 264)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_pp_split_tail(shape, xcd, monkeypatch):
+def test_pp_split_tail(shape, xcd, tile, monkeypatch):
     """The ping-pong kernel with its last round split over K (tile counts of
     6, 6, 272, 16, 12, 4, 16 and 64 on 256 CUs): exact on integer inputs, for
     every split tile, K tails and a mix of whole and split tiles; twice in a
     row, so the second call relies on fresh flag epochs.  Split-tile counts
     that are a multiple of 8 pair workgroups on one XCD (partials through its
     L2) unless MGEMM_PP_XCD=0; the others always pair across XCDs."""
-    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    monkeypatch.setenv("MGEMM_BF16_TILE", tile)
     monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
     monkeypatch.setenv("MGEMM_PP_XCD", xcd)
     tiles = -(-shape[0] // 256) * -(-shape[1] // 256)
     split_tiles = tiles % 256
-    want = "bf16_pp_256x256x32_splitk"
+    want = tile + "_splitk"
     if xcd == "1" and split_tiles % 8 == 0:
         want += "_xcd"
     for rep in range(2):
@@ -322,28 +326,31 @@ def test_pp_split_tail(shape, xcd, monkeypatch):
 
 
 def test_pp_split_alternating(monkeypatch):
-    """Split calls alternating between XCD-local and cross-XCD pairs, and
-    between shapes, share the flag epochs of one stream: every call exact."""
-    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    """Split calls alternating between the two 256 x 256 kernels, between
+    XCD-local and cross-XCD pairs, and between shapes, share the flag epochs
+    of one stream: every call exact."""
     monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
-    plan = [((1024, 4096, 264), "1"), ((1024, 4096, 264), "0"), ((512, 2048, 328), "1"),
-            ((500, 712, 320), "1"), ((1024, 4096, 264), "1"), ((512, 2048, 328), "0")]
-    for i, (shape, xcd) in enumerate(plan):
+    plan = [((1024, 4096, 264), "1", 0), ((1024, 4096, 264), "0", 1), ((512, 2048, 328), "1", 1),
+            ((500, 712, 320), "1", 0), ((1024, 4096, 264), "1", 1), ((512, 2048, 328), "0", 0),
+            ((500, 712, 320), "0", 1), ((1024, 4096, 264), "1", 0)]
+    for i, (shape, xcd, k) in enumerate(plan):
         monkeypatch.setenv("MGEMM_PP_XCD", xcd)
+        monkeypatch.setenv("MGEMM_BF16_TILE", SPLIT_TILES[k])
         case = make_case(*shape, "bf16", 1.0, 0.5, "i:4", "i:4", "i:4", seed=60 + i)
         C, name = run(case)
-        assert name.startswith("bf16_pp_256x256x32_splitk"), name
+        assert name.startswith(SPLIT_TILES[k] + "_splitk"), name
         Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.0, 0.5, bf16=True)
         assert np.array_equal(C.astype(np.float64), Cref), (i, shape, xcd)
 
 
-def test_pp_split_off(monkeypatch):
+@pytest.mark.parametrize("tile", SPLIT_TILES)
+def test_pp_split_off(tile, monkeypatch):
     """MGEMM_PP_SPLIT=0 keeps the whole-tile kernel on a shape that would split."""
-    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_pp_256x256x32")
+    monkeypatch.setenv("MGEMM_BF16_TILE", tile)
     monkeypatch.setenv("MGEMM_PP_SPLIT", "0")
     case = make_case(500, 712, 320, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=52)
     C, name = run(case)
-    assert name == "bf16_pp_256x256x32", name
+    assert name == tile, name
     Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=True)
     assert np.array_equal(C.astype(np.float64), Cref)
 
