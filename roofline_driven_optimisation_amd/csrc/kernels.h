@@ -77,6 +77,9 @@ constexpr int kSkinnyCols = 128;  // output columns per workgroup
 // Split count for the decode shapes; `xcd_local` picks the rule for the
 // XCD-local reduction (launch_skinny_bf16_xcd), whose partials are cheaper.
 int skinny_pick_splits(int M, int N, int K, int num_cus, bool xcd_local);
+// Whether each K-slice of B (and all of A) stays below 2^31 bytes, the reach
+// of the kernel's 32-bit buffer offsets, with `splits` slices.
+bool skinny_slice_fits(int M, int N, int K, int splits);
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
                               int *counters, int counter_ints, hipStream_t stream);

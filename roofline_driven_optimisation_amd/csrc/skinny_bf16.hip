@@ -364,6 +364,14 @@ int skinny_pick_splits(int M, int N, int K, int num_cus, bool xcd_local) {
     return splits;
 }
 
+bool skinny_slice_fits(int M, int N, int K, int splits) {
+    const int kblks = (K + kKBlock - 1) / kKBlock;
+    if (splits < 1) splits = 1;
+    const int per = (kblks + splits - 1) / splits > 0 ? (kblks + splits - 1) / splits : 1;
+    return static_cast<long long>(per) * kKBlock * N * 2 < 0x7fff0000LL &&
+           static_cast<long long>(M) * K * 2 < 0x7fff0000LL;
+}
+
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
                               int *counters, int counter_ints, hipStream_t stream) {

@@ -433,3 +433,34 @@ def test_dispatch_names():
             assert name == want
         else:
             assert name.startswith(("bf16_mfma_", "bf16_pp_", "bf16_q4_"))
+
+
+def test_skinny_b_over_2gib(gpu):
+    """A decode-shaped GEMM whose B exceeds 2 GiB (1 x 16384 x 65544 bf16:
+    2.15 GB, as large LM heads are): one split would make a K-slice too
+    large for 32-bit buffer offsets, so the library must raise the split
+    count rather than fail.  Integer entries, sampled outputs (every column
+    block edge and the ragged last block included) compared exactly with
+    the oracle; B is generated on the GPU from a seeded torch generator and
+    copied to the host for the oracle."""
+    torch = gpu
+    from gpu_helpers import sample_positions
+    M, K, N = 1, 16384, 65544
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    Bd = torch.randint(-2, 3, (K, N), dtype=torch.int8, device="cuda", generator=g)
+    Bd = Bd.to(torch.bfloat16)
+    A = make_case(M, 8, K, "bf16", 1.0, 0.0, "i:2", "i:2", seed=32).A  # M x K bf16 bits
+    Ad = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).cuda()
+    Cd = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    log("  gpu 1x65544x16384 bf16, B of %.2f GB" % (K * N * 2 / 1e9))
+    binding.gemm(Ad, Bd, Cd, 1.0, 0.0)
+    name = binding.last_kernel()
+    torch.cuda.synchronize()
+    assert name.startswith("skinny_bf16_splitk"), name
+    rows, cols = sample_positions(M, N, 2048, seed=3)
+    Bh = Bd.view(torch.int16).cpu().numpy().view(np.uint16)
+    del Bd
+    ref, _ = oracle.gemm_entries(A, Bh, rows, cols, None, 1.0, 0.0, bf16=True)
+    got = Cd.cpu().numpy()[rows, cols].astype(np.float64)
+    assert np.array_equal(got, ref)
