@@ -887,7 +887,8 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
 //     sub-step 0 (with the reads of sub-step 1), the first 8 MFMAs of
 //     sub-step 1, a wait and a barrier.  An iteration ends at the barrier,
 //     where no LDS read is outstanding, so the compiler's wait counts inside
-//     the body are exact; reads are issued in the order the MFMAs use them;
+//     the body are exact; reads are issued in the order the MFMAs use them
+//     (consecutive MFMAs share a B fragment);
 //   * the eight 1 KB copies of step t + 3 are spread over the step, one per
 //     four MFMAs in sub-step 0 and one per two after it.  Issuing them in a
 //     burst stalled the MFMA stream behind the copy queue (timing-only copies
@@ -1007,9 +1008,10 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
             for (int e = 0; e < 4; ++e) b[jj][4 * r + e] = part[e];
         }
     };
-    // reads in consumption order: A block 0, all B blocks, the other A blocks
+    // reads in consumption order: B block 0 (two halves), every A block,
+    // then the other B blocks
     auto read_in_order = [&](int stage, int s, int r, bf16x8 (&a)[MI], s16x8 (&b)[NI]) {
-        const int q = r == 0 ? 0 : (r <= 2 * NI ? MI + r - 1 : r - 2 * NI);
+        const int q = r < 2 ? MI + r : (r < 2 + MI ? r - 2 : r);
         read_one(stage, s, q, a, b);
     };
 
@@ -1022,13 +1024,15 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
     bf16x8 fa[2][MI];
     s16x8 fb[2][NI];
+    // MFMA q of a sub-step is block (q % MI, q / MI): consecutive MFMAs
+    // share their B fragment (measured 0.5 % faster than sharing A)
     auto mfma = [&](int q, int f) {
-        const int i = q / NI, jj = q % NI;
+        const int jj = q / MI, i = q % MI;
         acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, fb[f][jj]), fa[f][i], acc[i][jj], 0, 0, 0);
     };
     constexpr int kMfma = MI * NI;
-    constexpr int kEarly = 2 * NI;
+    constexpr int kEarly = 2 * MI;
     constexpr int kTail = kMfma - kEarly;
     // vmcnt <= vm and lgkmcnt == 0
     constexpr int kWaitSteady = (2 * COPIES & 15) | (7 << 4) | ((2 * COPIES >> 4) << 14);
