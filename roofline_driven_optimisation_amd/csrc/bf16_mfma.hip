@@ -79,13 +79,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 64;
-// An offset past every descriptor range (all ranges are clamped below 2^31).
-// Buffer builtins take the offset as int: always pass static_cast<int>(...).
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <int BM, int BN>
 struct Tile {
@@ -109,54 +104,6 @@ __device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
 
 // Swizzle key of A row r (see the layout notes above).
 __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes) {
-    if (bytes < 0) bytes = 0;
-    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             kRsrcFlags);
-}
-
-// The same raw-buffer descriptor as four dwords (base, stride 0, range, flags).
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 make_desc(const void *base, long long bytes) {
-    if (bytes < 0) bytes = 0;
-    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    i32x4 d;
-    d.x = static_cast<int>(static_cast<uint32_t>(p));
-    d.y = static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu);
-    d.z = static_cast<int>(bytes);
-    d.w = kRsrcFlags;
-    return d;
-}
-
-// One direct global -> LDS copy: 16 bytes per lane from byte offset `voff`
-// of the buffer `desc` into LDS at `lds_addr` + 16 * lane.  sc0 makes the
-// load bypass the vector L1 (the data is used once per workgroup and lands
-// in LDS; about 4% faster on the square GEMM than a cached load).  Written as inline
-// assembly on purpose: the compiler then does not model it as an LDS write
-// and does not stall the fragment reads of the other stage behind it (it
-// cannot prove the two stages apart); the K loop waits for these copies
-// explicitly (s_waitcnt + barrier) before reading the stage they fill.  M0
-// holds the LDS address for the instruction and is restored afterwards; the
-// s_nop is the wait state required between an M0 write and an LDS DMA.
-__device__ __forceinline__ void lds_dma16(i32x4 desc, uint32_t lds_addr, uint32_t voff) {
-    int saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen sc0 lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_addr), "v"(voff), "s"(desc)
-        : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p));
-}
 
 // Epilogue of one wave: C = alpha * acc + beta * C for MI x NI blocks of 32 x
 // 32.  The MFMAs take the B fragment as their first operand and the A

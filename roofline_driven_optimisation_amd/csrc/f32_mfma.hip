@@ -1,4 +1,7 @@
 // fp32 GEMM on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), LDS-tiled.
+// Two kernels share the tiling below: f32_dma_kernel (further down; direct
+// global -> LDS copies, the path for 16-byte aligned rows) and
+// f32_mfma_kernel (register-staged copies, any alignment and any size).
 //
 // Structure (page "Naive GEMM and Roofline analysis", section 10.4: block
 // tile -> warp tile -> matrix instruction, with double buffering):
@@ -202,6 +205,136 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
         }
 }
 
+// ---- direct-to-LDS kernel (16-byte aligned rows, K < 2^21, N < 2^22) -------
+// The same tiles, waves, MFMAs and fragment double-buffering as
+// f32_mfma_kernel, but the next K tile goes global -> LDS with direct copies
+// (lds_dma16: no staging registers, no LDS write instructions, no wait until
+// the end of the step), issued at the start of the step into the other
+// stage.  A direct copy writes 1 KB of LDS contiguously, so the padded
+// layouts above are replaced by XOR swizzles of 16-byte chunks:
+//   * A stage: 128 rows of 32 floats, chunk c of row m at position
+//     c ^ ((m / 2) % 8).  The 32 rows of a fragment read fall on 16 distinct
+//     bank groups (8 chunk positions x two row parities), a 2-way conflict;
+//   * B stage: 32 rows of 128 floats, chunk c of row k at c ^ (8 (k % 2)):
+//     rows 2s and 2s + 1 sit 32 banks apart, conflict-free as before.
+// Measured 4 % faster than register staging at 4096^3 and 4092^3 (1064-1070
+// against 1108-1116 us); spreading the copies over the step gained nothing.
+// Rows past M, B rows past K, and chunks past K (A) or N (B) read zeros.
+// A stage: 128 rows x 32 floats (8 chunks of 16 B per row), chunk c of row m
+// at position c ^ ((m >> 1) & 7).  B stage: 32 rows x 128 floats (32 chunks),
+// chunk c of row k at position c ^ (8 (k & 1)).
+__device__ __forceinline__ int swz_fa(int m) { return (m >> 1) & 7; }
+__device__ __forceinline__ int swz_fb(int k) { return (k & 1) << 3; }
+
+__global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int K, float alpha,
+                                                             float beta,
+                                                             const float *__restrict__ A,
+                                                             const float *__restrict__ B,
+                                                             float *C, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) float As[2][kBM * kBK];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kBK * kBN];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tm, tn);
+    const int m0 = tm * kBM, n0 = tn * kBN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // copies: A wave-load L = 4 q + wave covers rows 8 L .. 8 L + 7 (lane p:
+    // row 8 L + p / 8, position p % 8); B wave-load L covers rows 2 L, 2 L + 1
+    // (lane p: row 2 L + p / 32, position p % 32).
+    const int a_row = 8 * wave + (lane >> 3);             // + 32 q
+    const int a_lc = (lane & 7) ^ swz_fa(a_row);          // swz_fa(a_row + 32 q) = swz_fa(a_row)
+    const int b_row = 2 * wave + (lane >> 5);             // + 8 q
+    const int b_lc = (lane & 31) ^ swz_fb(b_row);
+    const bool b_col_ok = n0 + 4 * b_lc < N;
+    auto issue_tile = [&](int k0, int buf) {
+        const i32x4 ra = make_desc(A + static_cast<size_t>(m0) * K, static_cast<long long>(M - m0) * K * 4);
+        const i32x4 rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                                  (static_cast<long long>(K - k0) * N - n0) * 4);
+        const bool a_k_ok = k0 + 4 * a_lc < K;
+        const uint32_t la = lds_address(&As[buf][0]), lb = lds_address(&Bs[buf][0]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = a_row + 32 * q;
+            const uint32_t off = a_k_ok ? static_cast<uint32_t>((row * K + k0 + 4 * a_lc) * 4) : kOOB;
+            lds_dma16(ra, la + (4 * q + wave) * 1024, off);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = b_row + 8 * q;
+            const uint32_t off = b_col_ok ? static_cast<uint32_t>((row * N + 4 * b_lc) * 4) : kOOB;
+            lds_dma16(rb, lb + (4 * q + wave) * 1024, off);
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int ktiles = (K + kBK - 1) / kBK;
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ktiles; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < ktiles) issue_tile((t + 1) * kBK, cur ^ 1);
+        float fa[2][2], fb[2][2];
+        auto read_frags = [&](int s, int buf) {
+            const int kk = 2 * s + h;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int m = wm * 64 + 32 * i + l32;
+                fa[buf][i] = As[cur][m * kBK + (((kk >> 2) ^ swz_fa(m)) << 2) + (kk & 3)];
+                const int n = wn * 64 + 32 * i + l32;
+                fb[buf][i] = Bs[cur][kk * kBN + (((n >> 2) ^ swz_fb(kk)) << 2) + (n & 3)];
+            }
+        };
+        read_frags(0, 0);
+#pragma unroll
+        for (int s = 0; s < kBK / 2; ++s) {
+            const int buf = s & 1;
+            if (s + 1 < kBK / 2) read_frags(s + 1, buf ^ 1);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], fa[buf][0], acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], fa[buf][0], acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], fa[buf][1], acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], fa[buf][1], acc[1][1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // own copies of tile t+1 landed, own reads done
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = m0 + wm * 64 + 32 * i + l32;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * h;
+                if (row >= M || col >= N) continue;
+                float *c = C + static_cast<size_t>(row) * N + col;
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = alpha * acc[i][j][4 * g + e];
+                if (beta != 0.0f) {
+                    const f32x4 cin = *reinterpret_cast<const f32x4 *>(c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                }
+                *reinterpret_cast<f32x4 *>(c) = out;
+            }
+        }
+}
+
 }  // namespace
 
 const char *f32_mfma_name(bool vec) {
@@ -214,7 +347,11 @@ hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const f
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
-    if (vec)
+    if (vec && K < (1 << 21) && N < (1 << 22))
+        f32_dma_kernel<<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                  static_cast<int>(tiles_m),
+                                                  static_cast<int>(tiles_n));
+    else if (vec)
         f32_mfma_kernel<true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
                                                           static_cast<int>(tiles_m),
                                                           static_cast<int>(tiles_n));

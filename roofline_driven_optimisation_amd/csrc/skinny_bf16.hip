@@ -70,8 +70,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKBlock = 32;  // k rows per MFMA step
 constexpr int kDepth = 1;    // k-blocks per pipeline stage
-constexpr uint32_t kOOB = 0x80000000u;  // an offset past every descriptor range
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kNonTemporal = 2;         // buffer-load cache policy: streaming (nt)
 constexpr int kCounterLine = 32;        // ints per 128-byte line
 

@@ -30,6 +30,7 @@ KERNEL_SOURCES = {
     "bf16_pp": "bf16_mfma.hip",
     "bf16_q4": "bf16_mfma.hip",
     "f32_mfma": "f32_mfma.hip",
+    "f32_dma": "f32_mfma.hip",
     "skinny": "skinny_bf16.hip",
     "naive": "naive.hip",
 }

@@ -16,7 +16,7 @@ def test_code_hash_sees_code_changes():
 
 
 def test_source_hash_known_families():
-    for fam in ("bf16_q4", "bf16_pp", "bf16_mfma", "f32_mfma", "skinny", "naive"):
+    for fam in ("bf16_q4", "bf16_pp", "bf16_mfma", "f32_mfma", "f32_dma", "skinny", "naive"):
         h = source_hash(fam)
         assert len(h) == 16 and int(h, 16) >= 0
     assert source_hash("bf16_q4") == source_hash("bf16_pp")  # one source file
