@@ -206,25 +206,31 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
 }
 
 // ---- direct-to-LDS kernel (16-byte aligned rows, K < 2^21, N < 2^22) -------
-// The same tiles, waves, MFMAs and fragment double-buffering as
-// f32_mfma_kernel, but the next K tile goes global -> LDS with direct copies
-// (lds_dma16: no staging registers, no LDS write instructions, no wait until
-// the end of the step), issued at the start of the step into the other
-// stage.  A direct copy writes 1 KB of LDS contiguously, so the padded
-// layouts above are replaced by XOR swizzles of 16-byte chunks:
+// The same tiles, waves and MFMAs as f32_mfma_kernel, but:
+//   * the next K tile goes global -> LDS with direct copies (lds_dma16: no
+//     staging registers, no LDS write instructions, no wait until the end of
+//     the step), issued at the start of the step into the other stage;
+//   * MFMA k-pair s takes k = s from lanes 0-31 and k = 16 + s from lanes
+//     32-63 (any pairing of the 32 k of a step sums the same products).  A
+//     lane's A values for four consecutive pairs are then one 16-byte chunk,
+//     read once for four pairs;
+//   * MFMA block j's column c is C column wn 64 + 2 c + j, so a lane reads
+//     its two blocks' B values for a pair as one 8-byte load, and the
+//     epilogue interleaves the two blocks back into 8 consecutive columns.
+// A direct copy writes 1 KB of LDS contiguously, so the padded layouts above
+// are replaced by XOR swizzles of 16-byte chunks:
 //   * A stage: 128 rows of 32 floats, chunk c of row m at position
-//     c ^ ((m / 2) % 8).  The 32 rows of a fragment read fall on 16 distinct
-//     bank groups (8 chunk positions x two row parities), a 2-way conflict;
-//   * B stage: 32 rows of 128 floats, chunk c of row k at c ^ (8 (k % 2)):
-//     rows 2s and 2s + 1 sit 32 banks apart, conflict-free as before.
-// Measured 4 % faster than register staging at 4096^3 and 4092^3 (1064-1070
-// against 1108-1116 us); spreading the copies over the step gained nothing.
+//     c ^ ((m / 2) % 8): the 16 lanes served together by a 16-byte read fall
+//     on 16 distinct bank groups;
+//   * B stage: 32 rows of 128 floats, chunk c of row k at c ^ 8 ((k / 16) % 2):
+//     the two lane halves of a read (rows s and 16 + s) sit 32 banks apart.
+// Measured at 4096^3 against the register-staged kernel (1108-1116 us):
+// direct copies 1064-1070 us, plus the permuted k pairs 1012 us, plus the
+// B swizzle on k / 16 993-1000 us, plus the paired B reads 989 us (139
+// TFLOP/s).  Spreading the copies over the step gained nothing.
 // Rows past M, B rows past K, and chunks past K (A) or N (B) read zeros.
-// A stage: 128 rows x 32 floats (8 chunks of 16 B per row), chunk c of row m
-// at position c ^ ((m >> 1) & 7).  B stage: 32 rows x 128 floats (32 chunks),
-// chunk c of row k at position c ^ (8 (k & 1)).
 __device__ __forceinline__ int swz_fa(int m) { return (m >> 1) & 7; }
-__device__ __forceinline__ int swz_fb(int k) { return (k & 1) << 3; }
+__device__ __forceinline__ int swz_fb(int k) { return ((k >> 4) & 1) << 3; }
 
 __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int K, float alpha,
                                                              float beta,
@@ -249,8 +255,8 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
     const int a_row = 8 * wave + (lane >> 3);             // + 32 q
     const int a_lc = (lane & 7) ^ swz_fa(a_row);          // swz_fa(a_row + 32 q) = swz_fa(a_row)
     const int b_row = 2 * wave + (lane >> 5);             // + 8 q
-    const int b_lc = (lane & 31) ^ swz_fb(b_row);
-    const bool b_col_ok = n0 + 4 * b_lc < N;
+    // rows b_row + 8 q: swz_fb = 8 (q / 2) since b_row < 8
+    auto b_lc = [&](int q) { return (lane & 31) ^ ((q >> 1) << 3); };
     auto issue_tile = [&](int k0, int buf) {
         const i32x4 ra = make_desc(A + static_cast<size_t>(m0) * K, static_cast<long long>(M - m0) * K * 4);
         const i32x4 rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
@@ -266,7 +272,8 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int row = b_row + 8 * q;
-            const uint32_t off = b_col_ok ? static_cast<uint32_t>((row * N + 4 * b_lc) * 4) : kOOB;
+            const int lc = b_lc(q);
+            const uint32_t off = (n0 + 4 * lc < N) ? static_cast<uint32_t>((row * N + 4 * lc) * 4) : kOOB;
             lds_dma16(rb, lb + (4 * q + wave) * 1024, off);
         }
     };
@@ -286,45 +293,73 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
     for (int t = 0; t < ktiles; ++t) {
         const int cur = t & 1;
         if (t + 1 < ktiles) issue_tile((t + 1) * kBK, cur ^ 1);
-        float fa[2][2], fb[2][2];
-        auto read_frags = [&](int s, int buf) {
-            const int kk = 2 * s + h;
+        // k-pair s of the MFMAs takes k = s from lanes 0-31 and k = 16 + s
+        // from lanes 32-63 (any pairing of the 32 k sums the same products),
+        // so a lane's A values for four consecutive pairs are one 16-byte
+        // chunk: one read for four pairs.
+        f32x4 fa4[2];
+        float fb[2][2];
+        auto read_a = [&](int u) {  // pairs 4u .. 4u + 3
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int m = wm * 64 + 32 * i + l32;
-                fa[buf][i] = As[cur][m * kBK + (((kk >> 2) ^ swz_fa(m)) << 2) + (kk & 3)];
-                const int n = wn * 64 + 32 * i + l32;
-                fb[buf][i] = Bs[cur][kk * kBN + (((n >> 2) ^ swz_fb(kk)) << 2) + (n & 3)];
+                fa4[i] = *reinterpret_cast<const f32x4 *>(
+                    &As[cur][m * kBK + (((4 * h + u) ^ swz_fa(m)) << 2)]);
             }
         };
-        read_frags(0, 0);
+        // B: MFMA block j's column c is C column wn 64 + 2 c + j, so a lane
+        // reads its two blocks' B values as one 8-byte pair.
+        auto read_b = [&](int s, int buf) {
+            const int kk = 16 * h + s;
+            const int n = wn * 64 + 2 * l32;
+            typedef float f32x2v __attribute__((ext_vector_type(2)));
+            const f32x2v v = *reinterpret_cast<const f32x2v *>(
+                &Bs[cur][kk * kBN + (((n >> 2) ^ swz_fb(kk)) << 2) + (n & 3)]);
+            fb[buf][0] = v.x;
+            fb[buf][1] = v.y;
+        };
+        f32x4 fa_cur[2];
+        read_a(0);
+        read_b(0, 0);
 #pragma unroll
         for (int s = 0; s < kBK / 2; ++s) {
             const int buf = s & 1;
-            if (s + 1 < kBK / 2) read_frags(s + 1, buf ^ 1);
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], fa[buf][0], acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], fa[buf][0], acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], fa[buf][1], acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], fa[buf][1], acc[1][1], 0, 0, 0);
+            if ((s & 3) == 0) {
+                fa_cur[0] = fa4[0];
+                fa_cur[1] = fa4[1];
+                if (s + 4 < kBK / 2) read_a((s >> 2) + 1);
+            }
+            if (s + 1 < kBK / 2) read_b(s + 1, buf ^ 1);
+            const float a0 = fa_cur[0][s & 3], a1 = fa_cur[1][s & 3];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], a0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], a0, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][0], a1, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[buf][1], a1, acc[1][1], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0);  // own copies of tile t+1 landed, own reads done
         __syncthreads();
     }
 
+    // Epilogue: register 4 g + e of block (i, j) of lane l is C[row][col]
+    // with row = wm 64 + 32 i + l % 32 and col = wn 64 + 16 g + 8 (l / 32) +
+    // 2 e + j: the two blocks interleave into 8 consecutive columns.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+        const int row = m0 + wm * 64 + 32 * i + l32;
+        if (row >= M) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = m0 + wm * 64 + 32 * i + l32;
+        for (int g = 0; g < 4; ++g) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * h;
-                if (row >= M || col >= N) continue;
+            for (int half = 0; half < 2; ++half) {
+                const int col = n0 + wn * 64 + 16 * g + 8 * h + 4 * half;
+                if (col >= N) continue;
                 float *c = C + static_cast<size_t>(row) * N + col;
                 f32x4 out;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = alpha * acc[i][j][4 * g + e];
+                out[0] = alpha * acc[i][0][4 * g + 2 * half];
+                out[1] = alpha * acc[i][1][4 * g + 2 * half];
+                out[2] = alpha * acc[i][0][4 * g + 2 * half + 1];
+                out[3] = alpha * acc[i][1][4 * g + 2 * half + 1];
                 if (beta != 0.0f) {
                     const f32x4 cin = *reinterpret_cast<const f32x4 *>(c);
 #pragma unroll
@@ -333,6 +368,7 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
                 *reinterpret_cast<f32x4 *>(c) = out;
             }
         }
+    }
 }
 
 }  // namespace
