@@ -90,9 +90,12 @@ struct Stage {
 };
 
 // XCD_LOCAL selects the placement and scratch of the split-K reduction.
-// false: workgroup b is split b % splits of column block b / splits; the
-// partials of split s are the M x N matrix at partials + s M N and the counter
-// of block cb is at counters + cb * counter_stride, all in uncached memory.
+// false: workgroup b is split b / col_blocks of column block b % col_blocks
+// (consecutive workgroups, dealt to the XCDs in turn, take adjacent column
+// blocks: each XCD streams from all of B, which measured 4-7 % faster than
+// giving the splits of a block consecutive ids); the partials of split s are
+// the M x N matrix at partials + s M N and the counter of block cb is at
+// counters + cb * counter_stride, all in uncached memory.
 // true: with col_blocks = 8 q + r, the r trailing column blocks take the
 // first r * splits workgroups (rounded up to a multiple of 8 by idle ones) and
 // reduce as above.  Then the workgroups with b % 8 == x, which share one
@@ -124,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
         const int b = blockIdx.x;
         if (b < rest_groups) {
             if (b >= rest * splits) return;  // padding: exits before any barrier
-            cb = col_blocks - rest + b / splits;
-            sp = b % splits;
+            sp = b / rest;
+            cb = col_blocks - rest + (b - sp * rest);
         } else {
             // rest_groups % 8 == 0, so (b - rest_groups) % 8 == b % 8
             const int x = b % kXcdCount, j = (b - rest_groups) / kXcdCount;
@@ -146,8 +149,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
             partials = reinterpret_cast<float *>(blk + kSkinnyXcdCounterInts * sizeof(int));
         }
     } else {
-        cb = blockIdx.x / splits;
-        sp = blockIdx.x - cb * splits;
+        const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
+        sp = blockIdx.x / col_blocks;
+        cb = blockIdx.x - sp * col_blocks;
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;

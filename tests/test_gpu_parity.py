@@ -355,6 +355,23 @@ def test_pp_split_off(tile, monkeypatch):
     assert np.array_equal(C.astype(np.float64), Cref)
 
 
+@pytest.mark.parametrize("tile", SPLIT_TILES)
+@pytest.mark.parametrize("shift", [-1000, -3, 0, 3, 7, 1000])
+def test_pp_split_point(tile, shift, monkeypatch):
+    """The K step where a split pair divides its tile's K loop (half the
+    steps less MGEMM_PP_SPLIT_SHIFT, clamped to 1 .. steps - 1): exact on
+    integer inputs for uneven halves and both clamps, with a K tail (328 =
+    10 steps of 32 and 8)."""
+    monkeypatch.setenv("MGEMM_BF16_TILE", tile)
+    monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
+    monkeypatch.setenv("MGEMM_PP_SPLIT_SHIFT", str(shift))
+    case = make_case(520, 776, 328, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=53)
+    C, name = run(case)
+    assert name.startswith(tile + "_splitk"), name
+    Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=True)
+    assert np.array_equal(C.astype(np.float64), Cref)
+
+
 @pytest.mark.parametrize("group", [1, 2, 4, 5, 99])
 @pytest.mark.parametrize("shape", [(16, 11008, 4096), (1, 4096, 11008), (3, 1160, 2048)],
                          ids=lambda s: "x".join(map(str, s)))
