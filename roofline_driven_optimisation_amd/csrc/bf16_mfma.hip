@@ -125,25 +125,37 @@ __device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
     const bool read_c = beta != 0.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+        const int row = row0 + 32 * i + l32;
+        auto offset = [&](int jj, int g) {
+            const int col = col0 + 32 * jj + 8 * g + 4 * h;
+            return col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+        };
+        // The block row's C loads are all issued before its stores: the
+        // compiler cannot tell loads and stores of C apart, so a load placed
+        // after a store would wait for it.
+        f32x4 cin[NI][4];
+        if (read_c) {
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    cin[jj][g] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rc, static_cast<int>(offset(jj, g)), 0, 0));
+        }
 #pragma unroll
         for (int jj = 0; jj < NI; ++jj) {
-            const int row = row0 + 32 * i + l32;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = col0 + 32 * jj + 8 * g + 4 * h;
-                const uint32_t off =
-                    col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
                 f32x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) out[e] = alpha * acc[i][jj][4 * g + e];
                 if (read_c) {
-                    const f32x4 cin = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[jj][g][e], out[e]);
                 }
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
-                                                       static_cast<int>(off), 0, 0);
+                                                       static_cast<int>(offset(jj, g)), 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -194,38 +206,55 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
         }
         const int chunk = lane & 15;
         const int col = col0 + 4 * chunk;
+        // Rows in groups of kGroup: the group's global loads (partial, C)
+        // are all issued before its stores.  The compiler cannot tell the
+        // loaded buffers from the stored C apart, so a load placed after a
+        // store would wait for it: one memory round trip per row.
+        constexpr int kGroup = 8;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = 4 * j + (lane >> 4);
-            const f32x4 v =
-                *reinterpret_cast<const f32x4 *>(&region[r * 64 + ((chunk ^ (r & 15)) * 4)]);
-            const int row = row0 + 64 * half + r;
-            const int woff = ((row * ldw) + col0 + 4 * chunk) * 4;  // tile-local
-            if (MODE == kPostPartial) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw, woff, 0,
-                                                       0);
-                continue;
+        for (int j0 = 0; j0 < 16; j0 += kGroup) {
+            f32x4 pv[kGroup], cv[kGroup];
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int r = 4 * (j0 + u) + (lane >> 4);
+                const int row = row0 + 64 * half + r;
+                if (MODE == kAddPartial)
+                    pv[u] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rw, ((row * ldw) + col0 + 4 * chunk) * 4, 0, PLOAD));
+                if (MODE != kPostPartial && read_c) {
+                    const uint32_t off =
+                        col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                    cv[u] = __builtin_bit_cast(
+                        f32x4,
+                        __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
+                }
             }
-            const uint32_t off =
-                col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
-            f32x4 out;
-            if (MODE == kAddPartial) {
-                const f32x4 p = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, PLOAD));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = alpha * (v[e] + p[e]);
-            } else {
+            for (int u = 0; u < kGroup; ++u) {
+                const int r = 4 * (j0 + u) + (lane >> 4);
+                const f32x4 v =
+                    *reinterpret_cast<const f32x4 *>(&region[r * 64 + ((chunk ^ (r & 15)) * 4)]);
+                const int row = row0 + 64 * half + r;
+                if (MODE == kPostPartial) {
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, v), rw, ((row * ldw) + col0 + 4 * chunk) * 4,
+                        0, 0);
+                    continue;
+                }
+                const uint32_t off =
+                    col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                f32x4 out;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
+                for (int e = 0; e < 4; ++e)
+                    out[e] = alpha * (MODE == kAddPartial ? v[e] + pv[u][e] : v[e]);
+                if (read_c) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cv[u][e], out[e]);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
+                                                       static_cast<int>(off), 0, 0);
             }
-            if (read_c) {
-                const f32x4 cin = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
-            }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
-                                                   static_cast<int>(off), 0, 0);
         }
     }
 }
@@ -262,35 +291,44 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
             }
         const int chunk = lane & 31;
         const int col = col0 + 4 * chunk;
+        // All 16 rows' global loads (partial, C) are issued before any
+        // store: the compiler cannot tell the loaded buffers from the stored
+        // C apart, so a load placed after a store would wait for it.
+        f32x4 pv[16], cv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int row = row0 + 32 * i + 2 * j + h;
+            if (MODE == kAddPartial)
+                pv[j] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (row * ldw + col) * 4, 0,
+                                                                 PLOAD));
+            if (MODE != kPostPartial && read_c) {
+                const uint32_t off =
+                    col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                cv[j] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int r = 2 * j + h;
             const f32x4 v =
                 *reinterpret_cast<const f32x4 *>(&region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
             const int row = row0 + 32 * i + r;
-            const int woff = (row * ldw + col) * 4;  // tile-local
             if (MODE == kPostPartial) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw, woff, 0,
-                                                       0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw,
+                                                       (row * ldw + col) * 4, 0, 0);
                 continue;
             }
             const uint32_t off =
                 col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
             f32x4 out;
-            if (MODE == kAddPartial) {
-                const f32x4 pp = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, PLOAD));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = alpha * (v[e] + pp[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = alpha * v[e];
-            }
+            for (int e = 0; e < 4; ++e)
+                out[e] = alpha * (MODE == kAddPartial ? v[e] + pv[j][e] : v[e]);
             if (read_c) {
-                const f32x4 cin = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cv[j][e], out[e]);
             }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
                                                    static_cast<int>(off), 0, 0);
@@ -1120,9 +1158,8 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 // Relative per-CU speed of each tile configuration at equal occupancy,
 // measured on the square and prefill shapes (the 128 x 128 tile is the
 // unit).  At 4096^3 the four-wave 256 x 256 kernel ran 0.5-2.7 us ahead of
-// the ping-pong kernel on three boards out of four; a shape that leaves a
-// last round at most half full still goes to the ping-pong kernel, whose
-// split of that round (costed in the picker) is worth more.
+// the ping-pong kernel on three boards out of four, and with a split last
+// round 1.5-4 us ahead on the four 2048-row prefill shapes.
 const double kTileEfficiency[kNumConfigs] = {1.29, 0.85, 0.85, 1.0, 1.27};
 // LDS bytes per workgroup, which set how many workgroups share a CU.
 int tile_lds_bytes(int c) {
@@ -1241,12 +1278,9 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
         const long long full = wgs / slots, rem = wgs % slots;
         double rounds =
             static_cast<double>(full) + (rem ? 0.5 + 0.5 * static_cast<double>(rem) / slots : 0.0);
-        // a split last round: half the K steps on twice the CUs, plus the
-        // exchange of partial tiles
-        // (the four-wave kernel can split too, but measured no better on the
-        // prefill shapes and 8 % slower where every tile splits at K = 4096,
-        // so it is costed unsplit)
-        if (allow_split && c == bf16_pp_config() && bf16_pp_split_tiles(M, N, K, num_cus) > 0)
+        // a split last round (either 256 x 256 kernel): half the K steps on
+        // twice the CUs, plus the exchange of partial tiles
+        if (allow_split && bf16_config_splits(c) && bf16_pp_split_tiles(M, N, K, num_cus) > 0)
             rounds = static_cast<double>(full) + 0.6;
         const double cost = rounds * occ * bm * bn / kTileEfficiency[c];
         if (c == 0 || cost < best_cost) {

@@ -170,6 +170,24 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
     // with row = wm 64 + 32 i + l % 32 and col = wn 64 + 32 j + 8 g + 4 (l / 32).
     // With VEC (N % 4 == 0) a 4-column group is wholly inside or outside C
     // and C rows are 16-byte aligned when C is, which the caller checked.
+    // With VEC and beta != 0 every C load is issued before the first store
+    // (a load the compiler placed after a store to C would wait for it).
+    f32x4 cin[2][2][4];
+    if (VEC && beta != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = m0 + wm * 64 + 32 * i + l32;
+                    const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * h;
+                    cin[i][j][g] =
+                        (row < M && col < N)
+                            ? *reinterpret_cast<const f32x4 *>(C + static_cast<size_t>(row) * N + col)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -186,9 +204,8 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = alpha * acc[i][j][4 * g + e];
                     if (beta != 0.0f) {
-                        const f32x4 cin = *reinterpret_cast<const f32x4 *>(c);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                        for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[i][j][g][e], out[e]);
                     }
                     *reinterpret_cast<f32x4 *>(c) = out;
                 } else {
@@ -343,7 +360,26 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
 
     // Epilogue: register 4 g + e of block (i, j) of lane l is C[row][col]
     // with row = wm 64 + 32 i + l % 32 and col = wn 64 + 16 g + 8 (l / 32) +
-    // 2 e + j: the two blocks interleave into 8 consecutive columns.
+    // 2 e + j: the two blocks interleave into 8 consecutive columns.  With
+    // beta != 0 every C load is issued before the first store: the compiler
+    // cannot tell the loads from the stores to C apart, so a load placed
+    // after a store would wait for it (one memory round trip per store).
+    f32x4 cin[2][4][2];
+    if (beta != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int row = m0 + wm * 64 + 32 * i + l32;
+                    const int col = n0 + wn * 64 + 16 * g + 8 * h + 4 * half;
+                    cin[i][g][half] =
+                        (row < M && col < N)
+                            ? *reinterpret_cast<const f32x4 *>(C + static_cast<size_t>(row) * N + col)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = m0 + wm * 64 + 32 * i + l32;
@@ -361,9 +397,8 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
                 out[2] = alpha * acc[i][0][4 * g + 2 * half + 1];
                 out[3] = alpha * acc[i][1][4 * g + 2 * half + 1];
                 if (beta != 0.0f) {
-                    const f32x4 cin = *reinterpret_cast<const f32x4 *>(c);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[e], out[e]);
+                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[i][g][half][e], out[e]);
                 }
                 *reinterpret_cast<f32x4 *>(c) = out;
             }
