@@ -9,6 +9,9 @@ The definition it follows is the GEMM formula of page "Naive GEMM and
 Roofline analysis", section 10.1, with the row-major indexing of that page's
 naive kernel (section 10.2).  Every function returns the fp64 result together
 with the parity denominator ``|alpha| * sum_k |A*B| + |beta*C_in| + 1e-30``.
+The optional fused epilogue (bias over the N columns, then an activation)
+follows the Linear layer Y = XW + b of page "From model computation to GPU
+execution", section 1.1.
 """
 from __future__ import annotations
 
@@ -58,6 +61,8 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = [i64, i64, i64, f64, f64, vp, vp, vp, i64, vp, vp, vp, vp]
             fn.restype = ctypes.c_int
+        lib.oracle_epilogue.argtypes = [i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp]
+        lib.oracle_epilogue.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -84,11 +89,52 @@ class Oracle:
             C = None  # never read when beta == 0
         return A, B, C, M, N, K
 
-    def gemm(self, A, B, C=None, alpha=1.0, beta=0.0, bf16=False):
+    def epilogue(self, z, den, bias=None, act=0, cols=None):
+        """Fused Linear-layer epilogue y = act(z + bias[n]) on a GEMM result z
+        (fp64, with its denominator den): returns (y, den_out), den_out being
+        the activation's slope bound times (den + |bias[n]|).  ``cols`` gives
+        each entry's column for sampled entries; None means z is a full
+        row-major matrix whose last axis is N.  act: 0 identity, 1 ReLU,
+        2 GELU (erf form), 3 SiLU."""
+        z = np.ascontiguousarray(z, dtype=np.float64)
+        den = np.ascontiguousarray(den, dtype=np.float64)
+        if z.shape != den.shape:
+            raise ValueError("z and den differ in shape")
+        if cols is None:
+            N = z.shape[-1] if z.ndim == 2 else 0
+            if z.ndim != 2:
+                raise ValueError("a full result must be 2-D")
+        else:
+            cols = np.ascontiguousarray(cols, dtype=np.int64)
+            if cols.shape != z.shape or z.ndim != 1:
+                raise ValueError("cols must match the sampled entries")
+            N = None
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+            if bias.ndim != 1:
+                raise ValueError("bias must be a vector")
+            if N is None:
+                N = bias.shape[0]
+            elif bias.shape[0] != N:
+                raise ValueError("bias must have N = %d entries" % N)
+        if N is None:
+            N = int(cols.max()) + 1 if cols.size else 1
+        y = np.empty_like(z)
+        den_out = np.empty_like(z)
+        rc = self.lib.oracle_epilogue(z.size, N, _ptr(cols), _ptr(z), _ptr(den), _ptr(bias),
+                                      int(act), _ptr(y), _ptr(den_out))
+        if rc != 0:
+            raise ValueError("oracle rejected the epilogue arguments (code %d)" % rc)
+        return y, den_out
+
+    def gemm(self, A, B, C=None, alpha=1.0, beta=0.0, bf16=False, bias=None, act=0):
         """Full fp64 reference: (C_ref, den), both float64 M x N arrays.
 
         ``bf16=True``: A and B are uint16 arrays of bf16 bit patterns,
         otherwise float32.  C is float32 and is read only when beta != 0.
+        With ``bias`` (fp32, N entries) or ``act`` the result is the fused
+        Linear-layer output act(alpha * A * B + beta * C + bias) and den the
+        matching epilogue denominator (see ``epilogue``).
         """
         A, B, C, M, N, K = self._operands(A, B, C, beta, bf16)
         Cref = np.empty((M, N), dtype=np.float64)
@@ -98,9 +144,12 @@ class Oracle:
                 _ptr(Cref), _ptr(den))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (code %d)" % rc)
+        if bias is not None or act:
+            return self.epilogue(Cref, den, bias, act)
         return Cref, den
 
-    def gemm_entries(self, A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False):
+    def gemm_entries(self, A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False,
+                     bias=None, act=0):
         """fp64 reference at the sampled positions (rows[e], cols[e]) only."""
         A, B, C, M, N, K = self._operands(A, B, C, beta, bf16)
         rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -114,6 +163,10 @@ class Oracle:
                 rows.shape[0], _ptr(rows), _ptr(cols), _ptr(out), _ptr(den))
         if rc != 0:
             raise ValueError("oracle rejected the arguments (code %d)" % rc)
+        if bias is not None or act:
+            if bias is not None and np.asarray(bias).shape != (N,):
+                raise ValueError("bias must have N = %d entries" % N)
+            return self.epilogue(out, den, bias, act, cols=cols)
         return out, den
 
     def num_threads(self) -> int:
@@ -132,12 +185,16 @@ def default() -> Oracle:
     return _default
 
 
-def gemm(A, B, C=None, alpha=1.0, beta=0.0, bf16=False):
-    return default().gemm(A, B, C, alpha, beta, bf16)
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, bf16=False, bias=None, act=0):
+    return default().gemm(A, B, C, alpha, beta, bf16, bias, act)
 
 
-def gemm_entries(A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False):
-    return default().gemm_entries(A, B, rows, cols, C, alpha, beta, bf16)
+def gemm_entries(A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False, bias=None, act=0):
+    return default().gemm_entries(A, B, rows, cols, C, alpha, beta, bf16, bias, act)
+
+
+def epilogue(z, den, bias=None, act=0, cols=None):
+    return default().epilogue(z, den, bias, act, cols)
 
 
 def num_threads() -> int:

@@ -181,6 +181,78 @@ int oracle_gemm_bf16_entries(int64_t M, int64_t N, int64_t K, double alpha, doub
     return gemm_entries(M, N, K, alpha, beta, A, B, ELEM_BF16, Cin, count, rows, cols, out, den);
 }
 
+/*
+ * Fused Linear-layer epilogue on a GEMM result.
+ *
+ * A Linear layer computes Y = XW + b (page "From model computation to GPU
+ * execution", section 1.1), and an elementwise function such as GELU is the
+ * typical consumer of its output (page "Where kernel performance comes
+ * from", sections on elementwise kernels and on fusing a GEMM with its
+ * elementwise epilogue).  Given z = alpha * A * B + beta * C_in from the
+ * functions above, this computes
+ *
+ *     y = act(z + bias[n])
+ *
+ * in fp64, with bias an fp32 vector over the N output columns (NULL: no
+ * bias) and act one of
+ *
+ *     0 identity   y = x
+ *     1 ReLU       y = 0 for x < 0, else x   (NaN stays NaN)
+ *     2 GELU       y = x * Phi(x) = x / 2 * erfc(-x / sqrt(2))
+ *     3 SiLU       y = x / (1 + exp(-x))
+ *
+ * Entry e is column cols[e] (cols == NULL: column e % N, a full row-major
+ * matrix).  The returned denominator is den_out[e] = slope * (den[e] +
+ * |bias[n]|): an error e_z in z moves y by at most slope * e_z, where slope
+ * bounds |act'| (1 for identity and ReLU; GELU' peaks at x = sqrt(2) at
+ * 1.1289, SiLU' near x = 2.40 at 1.0998; 1.13 and 1.10 are used), so the
+ * parity test |y_gpu - y| / den_out <= tol keeps the meaning it has for
+ * plain GEMM.
+ */
+static double act_fn(int act, double x)
+{
+    switch (act) {
+    case 1:
+        return x < 0.0 ? 0.0 : x;
+    case 2:
+        return 0.5 * x * erfc(-x / sqrt(2.0)); /* Phi(x) without the 1 + erf cancellation */
+    case 3:
+        return x / (1.0 + exp(-x));
+    default:
+        return x;
+    }
+}
+
+static double act_slope(int act)
+{
+    return act == 2 ? 1.13 : act == 3 ? 1.10 : 1.0;
+}
+
+int oracle_epilogue(int64_t count, int64_t N, const int64_t *cols, const double *z,
+                    const double *den, const float *bias, int act, double *y, double *den_out)
+{
+    if (count < 0 || N < 0 || act < 0 || act > 3)
+        return ORACLE_EINVAL;
+    if (count == 0)
+        return ORACLE_OK;
+    if (N == 0 || z == NULL || den == NULL || y == NULL || den_out == NULL)
+        return ORACLE_EINVAL;
+    if (cols != NULL)
+        for (int64_t e = 0; e < count; ++e)
+            if (cols[e] < 0 || cols[e] >= N)
+                return ORACLE_EINVAL;
+    const double slope = act_slope(act);
+    int64_t e;
+#pragma omp parallel for schedule(static)
+    for (e = 0; e < count; ++e) {
+        int64_t n = cols != NULL ? cols[e] : e % N;
+        double b = bias != NULL ? (double)bias[n] : 0.0;
+        y[e] = act_fn(act, z[e] + b);
+        den_out[e] = slope * (den[e] + fabs(b));
+    }
+    return ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_num_threads(void)
 {

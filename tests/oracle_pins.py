@@ -189,11 +189,88 @@ def pin_den_bounds_result(o):
     assert np.allclose(got, den, rtol=1e-15, atol=1e-29)
 
 
+def pin_epilogue_closed_forms(o):
+    """Activations against closed forms and independent library routines:
+    ReLU by sign; GELU(x) = x * Phi(x) with Phi from scipy.special.ndtr and
+    the table value Phi(1) = 0.8413447460685429; SiLU(x) = x * expit(x);
+    for both, f(x) - f(-x) = x (since Phi(x) + Phi(-x) = 1 and likewise for
+    the logistic function)."""
+    from scipy.special import expit, ndtr
+    x = np.array([[-6.0, -3.0, -1.0, -0.5, 0.0, 0.25, 1.0, 2.5, 7.0]])
+    one = np.ones_like(x)
+    y, _ = o.epilogue(x, one, None, 1)
+    assert np.array_equal(y, np.where(x < 0, 0.0, x))
+    y, _ = o.epilogue(x, one, None, 2)
+    assert np.allclose(y, x * ndtr(x), rtol=1e-14, atol=1e-300)
+    assert abs(o.epilogue(np.array([[1.0]]), np.ones((1, 1)), None, 2)[0][0, 0]
+               - 0.8413447460685429) < 1e-15
+    yn, _ = o.epilogue(-x, one, None, 2)
+    assert np.allclose(y - yn, x, rtol=1e-14, atol=1e-14)
+    y, _ = o.epilogue(x, one, None, 3)
+    assert np.allclose(y, x * expit(x), rtol=1e-14, atol=1e-300)
+    yn, _ = o.epilogue(-x, one, None, 3)
+    assert np.allclose(y - yn, x, rtol=1e-14, atol=1e-14)
+    y, _ = o.epilogue(x, one, None, 0)
+    assert np.array_equal(y, x)
+
+
+def pin_epilogue_bias_columns(o):
+    """The bias vector runs along the N columns of a row-major result, and
+    the denominator grows by |bias[n]|."""
+    z = np.arange(15, dtype=np.float64).reshape(3, 5) - 7.0
+    den = np.full_like(z, 2.0)
+    bias = np.array([0.5, -1.0, 2.0, -4.0, 8.0], dtype=np.float32)
+    y, d = o.epilogue(z, den, bias, 0)
+    assert np.array_equal(y, z + bias.astype(np.float64)[None, :])
+    assert np.array_equal(d, den + np.abs(bias.astype(np.float64))[None, :])
+    y, d = o.epilogue(z[1], den[1], bias, 1, cols=np.arange(5))
+    assert np.array_equal(y, np.maximum(z[1] + bias, 0.0))
+
+
+def pin_epilogue_gemm(o):
+    """Through gemm(): K = 0 gives act(beta * C + bias); the fused result of
+    a small integer product equals the epilogue applied to the plain one; and
+    sampled entries agree with the full matrix."""
+    C = _mat([[1, -2, 3], [-4, 5, -6]])
+    bias = np.array([1.0, 1.5, -2.0], dtype=np.float32)
+    y, _ = o.gemm(np.zeros((2, 0), np.float32), np.zeros((0, 3), np.float32), C, 1.0, 0.5,
+                  bias=bias, act=1)
+    assert np.array_equal(y, np.maximum(0.5 * C.astype(np.float64) + bias, 0.0))
+    A = _mat([[1, 2], [3, -4]])
+    B = _mat([[5, -6, 7], [8, 9, -1]])
+    z, den = o.gemm(A, B)
+    y, d = o.gemm(A, B, bias=bias, act=3)
+    y2, d2 = o.epilogue(z, den, bias, 3)
+    assert np.array_equal(y, y2) and np.array_equal(d, d2)
+    rows, cols = np.array([1, 0, 1]), np.array([2, 0, 1])
+    ye, de = o.gemm_entries(A, B, rows, cols, bias=bias, act=2)
+    yf, df = o.gemm(A, B, bias=bias, act=2)
+    assert np.array_equal(ye, yf[rows, cols]) and np.array_equal(de, df[rows, cols])
+
+
+def pin_epilogue_slope(o):
+    """The denominator's slope factor bounds |act'| everywhere: GELU' =
+    Phi(x) + x phi(x) and SiLU' = s(x) (1 + x (1 - s(x))) on a fine grid stay
+    below the factors 1.13 and 1.10 the oracle applies (1 for ReLU)."""
+    from scipy.special import expit, ndtr
+    x = np.linspace(-20, 20, 400001)
+    gelu_d = ndtr(x) + x * np.exp(-x * x / 2) / np.sqrt(2 * np.pi)
+    s = expit(x)
+    silu_d = s * (1 + x * (1 - s))
+    one = np.ones((1, 1))
+    for act, deriv in [(2, gelu_d), (3, silu_d)]:
+        _, d = o.epilogue(np.zeros((1, 1)), one, None, act)
+        assert np.max(np.abs(deriv)) <= d[0, 0] < np.max(np.abs(deriv)) + 0.01, act
+    _, d = o.epilogue(np.zeros((1, 1)), one, None, 1)
+    assert d[0, 0] == 1.0
+
+
 ALL_PINS = [
     pin_hand_signs, pin_rectangular_hand, pin_identity_zero_permutation, pin_all_ones,
     pin_alpha_beta_linearity, pin_transpose_identity, pin_brute_force_integers,
     pin_random_floats_vs_numpy, pin_bf16_widening, pin_beta_zero_reads_no_c, pin_k_zero,
     pin_entries_match_full, pin_entries_hand, pin_den_bounds_result,
+    pin_epilogue_closed_forms, pin_epilogue_bias_columns, pin_epilogue_gemm, pin_epilogue_slope,
 ]
 
 
@@ -216,6 +293,14 @@ MUTANTS = {
     "entries_b_transposed": ("load_elem(B, kind, k * N + n);\n            acc +=",
                              "load_elem(B, kind, n * K + k);\n            acc +="),
     "entries_dropped_alpha": ("out[e] = alpha * acc + beta * c_in;", "out[e] = acc + beta * c_in;"),
+    "bias_by_row": ("int64_t n = cols != NULL ? cols[e] : e % N;",
+                    "int64_t n = cols != NULL ? cols[e] : (e / N) % N;"),
+    "bias_dropped": ("y[e] = act_fn(act, z[e] + b);", "y[e] = act_fn(act, z[e]);"),
+    "den_without_bias": ("den_out[e] = slope * (den[e] + fabs(b));", "den_out[e] = slope * den[e];"),
+    "slope_dropped": ("return act == 2 ? 1.13 : act == 3 ? 1.10 : 1.0;", "return 1.0;"),
+    "gelu_unscaled_erf": ("erfc(-x / sqrt(2.0))", "erfc(-x)"),
+    "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
+    "relu_leaky": ("return x < 0.0 ? 0.0 : x;", "return x < 0.0 ? 0.01 * x : x;"),
 }
 
 
