@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 1
+#define GEMM_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -99,6 +99,43 @@ GEMM_API int gemm_f32(int M, int N, int K, float alpha, float beta,
  */
 GEMM_API int gemm_bf16(int M, int N, int K, float alpha, float beta,
               const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/*
+ * Fused Linear-layer epilogue.  A Linear layer computes Y = XW + b (page
+ * "From model computation to GPU execution", section 1.1), and fusing the
+ * elementwise work that follows a GEMM into its epilogue keeps the
+ * intermediate out of HBM (page "Where kernel performance comes from",
+ * section on optimising memory-bound kernels).  These entry points compute
+ *
+ *     C = act(alpha * A * B + beta * C + bias[n])
+ *
+ * in the same kernels and with the same arguments, layouts, dispatch and
+ * error behaviour as gemm_f32 / gemm_bf16, plus:
+ *   bias        device pointer to N float32 values, one per column of C
+ *               (read-only, caller-owned), or NULL for no bias;
+ *   activation  one of enum gemm_activation, applied in fp32 after the bias:
+ *               GEMM_ACT_NONE  x;
+ *               GEMM_ACT_RELU  0 for x < 0, else x (NaN stays NaN);
+ *               GEMM_ACT_GELU  x * Phi(x), Phi the standard normal CDF
+ *                              (the erf form, computed through erfcf);
+ *               GEMM_ACT_SILU  x / (1 + exp(-x)).
+ *               Any other value returns GEMM_ERR_INVALID_ARG and launches
+ *               nothing.
+ * With K == 0 the result is act(beta * C + bias) (zeros plus bias when beta
+ * is 0).  bias == NULL with GEMM_ACT_NONE is exactly gemm_f32 / gemm_bf16.
+ */
+enum gemm_activation {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1,
+    GEMM_ACT_GELU = 2,
+    GEMM_ACT_SILU = 3
+};
+GEMM_API int gemm_f32_bias_act(int M, int N, int K, float alpha, float beta,
+                               const float *A, const float *B, float *C,
+                               const float *bias, int activation, void *stream);
+GEMM_API int gemm_bf16_bias_act(int M, int N, int K, float alpha, float beta,
+                                const uint16_t *A, const uint16_t *B, float *C,
+                                const float *bias, int activation, void *stream);
 
 /*
  * The unoptimised starting point of section 10.2 of page "Naive GEMM and

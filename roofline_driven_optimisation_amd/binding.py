@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libgemm.so"
 
 GEMM_OK = 0
+# enum gemm_activation
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
 _lock = threading.Lock()
 _lib = None
 
@@ -50,6 +52,10 @@ def library():
         for name in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16"):
             fn = getattr(lib, name)
             fn.argtypes = [i, i, i, f, f, vp, vp, vp, vp]
+            fn.restype = ctypes.c_int
+        for name in ("gemm_f32_bias_act", "gemm_bf16_bias_act"):
+            fn = getattr(lib, name)
+            fn.argtypes = [i, i, i, f, f, vp, vp, vp, vp, i, vp]
             fn.restype = ctypes.c_int
         lib.gemm_status_string.argtypes = [ctypes.c_int]
         lib.gemm_status_string.restype = ctypes.c_char_p
@@ -102,16 +108,25 @@ def _check(A, B, C, in_dtype):
     return int(M), int(N), int(K)
 
 
-def _call(fn_name, A, B, C, alpha, beta, stream, in_dtype):
+def _call(fn_name, A, B, C, alpha, beta, stream, in_dtype, epilogue=None):
     import torch
     M, N, K = _check(A, B, C, in_dtype)
     lib = library()
+    extra = ()
+    if epilogue is not None:
+        bias, act = epilogue
+        if bias is not None:
+            if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32:
+                raise TypeError("bias must be a float32 tensor")
+            if bias.device != C.device or tuple(bias.shape) != (N,) or not bias.is_contiguous():
+                raise ValueError("bias must be a contiguous vector of N = %d on C's device" % N)
+        extra = (ctypes.c_void_p(bias.data_ptr() if bias is not None else 0), int(act))
     with torch.cuda.device(C.device):
         status = getattr(lib, fn_name)(M, N, K, float(alpha), float(beta),
                                        ctypes.c_void_p(A.data_ptr()),
                                        ctypes.c_void_p(B.data_ptr()),
                                        ctypes.c_void_p(C.data_ptr()),
-                                       _stream_handle(stream))
+                                       *extra, _stream_handle(stream))
     if status != GEMM_OK:
         raise GemmError(status, _status_message(status))
     return C
@@ -127,6 +142,24 @@ def gemm_bf16(A, B, C, alpha=1.0, beta=0.0, stream=None):
     """C = alpha*A@B + beta*C with bfloat16 A and B, float32 C."""
     import torch
     return _call("gemm_bf16", A, B, C, alpha, beta, stream, torch.bfloat16)
+
+
+def gemm_f32_bias_act(A, B, C, bias=None, activation=ACT_NONE, alpha=1.0, beta=0.0,
+                      stream=None):
+    """C = act(alpha*A@B + beta*C + bias) with float32 operands; bias is a
+    float32 vector over the N columns or None."""
+    import torch
+    return _call("gemm_f32_bias_act", A, B, C, alpha, beta, stream, torch.float32,
+                 (bias, activation))
+
+
+def gemm_bf16_bias_act(A, B, C, bias=None, activation=ACT_NONE, alpha=1.0, beta=0.0,
+                       stream=None):
+    """C = act(alpha*A@B + beta*C + bias) with bfloat16 A and B, float32 C
+    and bias."""
+    import torch
+    return _call("gemm_bf16_bias_act", A, B, C, alpha, beta, stream, torch.bfloat16,
+                 (bias, activation))
 
 
 def gemm_naive_f32(A, B, C, alpha=1.0, beta=0.0, stream=None):

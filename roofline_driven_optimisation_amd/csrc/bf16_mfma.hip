@@ -115,11 +115,14 @@ __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
 // element of C, so rows past M fall outside it; a 4-column group past N
 // (N is a multiple of 8, so a group is entirely inside or outside) is
 // redirected out of range.  Stores of one block are issued before the next
-// block is converted, which bounds the registers in use.
-template <int MI, int NI>
+// block is converted, which bounds the registers in use.  With EPI the fused
+// epilogue follows alpha/beta: act(x + bias[col]), `bias` based at the tile's
+// first column.
+template <int MI, int NI, bool EPI = false>
 __device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
                                              __amdgpu_buffer_rsrc_t rc, int row0, int col0,
-                                             int cols_left, int N, float alpha, float beta) {
+                                             int cols_left, int N, float alpha, float beta,
+                                             const float *bias = nullptr, int act = kActNone) {
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
     const bool read_c = beta != 0.0f;
@@ -154,6 +157,11 @@ __device__ __forceinline__ void store_c_tile(const f32x16 (&acc)[MI][NI],
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[jj][g][e], out[e]);
                 }
+                if constexpr (EPI) {
+                    const f32x4 bv = bias4<EPI>(bias, col0 + 32 * jj + 8 * g + 4 * h, cols_left);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], act);
+                }
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
                                                        static_cast<int>(offset(jj, g)), 0, 0);
             }
@@ -179,11 +187,13 @@ enum EpilogueMode { kStoreC, kPostPartial, kAddPartial };
 constexpr int kSystemScope = 1 | 16;  // buffer cache policy sc0 sc1: no stale L1 / L2 copy
 constexpr int kDeviceScope = 16;      // buffer cache policy sc1: no stale L1 copy
 
-template <int MI, int NI, EpilogueMode MODE, int PLOAD = kSystemScope>
+template <int MI, int NI, EpilogueMode MODE, int PLOAD = kSystemScope, bool EPI = false>
 __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], float *region,
                                                  __amdgpu_buffer_rsrc_t rc, int row0, int col0,
                                                  int cols_left, int N, float alpha, float beta,
-                                                 __amdgpu_buffer_rsrc_t rw, int ldw) {
+                                                 __amdgpu_buffer_rsrc_t rw, int ldw,
+                                                 const float *bias = nullptr,
+                                                 int act = kActNone) {
     static_assert(NI * 32 == 64 && MI % 2 == 0, "wave tile must be (64 k) x 64");
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
@@ -206,6 +216,7 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
         }
         const int chunk = lane & 15;
         const int col = col0 + 4 * chunk;
+        const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col, cols_left);
         // Rows in groups of kGroup: the group's global loads (partial, C)
         // are all issued before its stores.  The compiler cannot tell the
         // loaded buffers from the stored C apart, so a load placed after a
@@ -252,6 +263,8 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cv[u][e], out[e]);
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], act);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
                                                        static_cast<int>(off), 0, 0);
             }
@@ -268,12 +281,13 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
 // store instruction covers 8 whole 128-byte lines.  C = alpha * acc (+ beta
 // * C); same edge handling as store_c_tile.  MODE and PLOAD as for
 // store_c_tile_lds (a partial tile `rw` of ldw floats per row).
-template <int MI, EpilogueMode MODE = kStoreC, int PLOAD = kSystemScope>
+template <int MI, EpilogueMode MODE = kStoreC, int PLOAD = kSystemScope, bool EPI = false>
 __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], float *region,
                                                     __amdgpu_buffer_rsrc_t rc, int row0,
                                                     int col0, int cols_left, int N, float alpha,
                                                     float beta, __amdgpu_buffer_rsrc_t rw,
-                                                    int ldw) {
+                                                    int ldw, const float *bias = nullptr,
+                                                    int act = kActNone) {
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
     const bool read_c = beta != 0.0f;
@@ -291,58 +305,68 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
             }
         const int chunk = lane & 31;
         const int col = col0 + 4 * chunk;
-        // All 16 rows' global loads (partial, C) are issued before any
-        // store: the compiler cannot tell the loaded buffers from the stored
-        // C apart, so a load placed after a store would wait for it.
-        f32x4 pv[16], cv[16];
+        const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col, cols_left);
+        // The rows' global loads (partial, C) are issued a group at a time
+        // (all 16 rows; 8 with the fused epilogue, whose activation needs
+        // registers of its own) before the group's stores: the compiler
+        // cannot tell the loaded buffers from the stored C apart, so a load
+        // placed after a store would wait for it.
+        constexpr int kGroup = EPI ? 8 : 16;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int row = row0 + 32 * i + 2 * j + h;
-            if (MODE == kAddPartial)
-                pv[j] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (row * ldw + col) * 4, 0,
-                                                                 PLOAD));
-            if (MODE != kPostPartial && read_c) {
+        for (int j0 = 0; j0 < 16; j0 += kGroup) {
+            f32x4 pv[kGroup], cv[kGroup];
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int row = row0 + 32 * i + 2 * (j0 + u) + h;
+                if (MODE == kAddPartial)
+                    pv[u] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (row * ldw + col) * 4, 0,
+                                                                     PLOAD));
+                if (MODE != kPostPartial && read_c) {
+                    const uint32_t off =
+                        col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                    cv[u] = __builtin_bit_cast(
+                        f32x4,
+                        __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int r = 2 * (j0 + u) + h;
+                const f32x4 v =
+                    *reinterpret_cast<const f32x4 *>(&region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
+                const int row = row0 + 32 * i + r;
+                if (MODE == kPostPartial) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw,
+                                                           (row * ldw + col) * 4, 0, 0);
+                    continue;
+                }
                 const uint32_t off =
                     col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
-                cv[j] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, static_cast<int>(off), 0, 0));
-            }
-        }
+                f32x4 out;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = 2 * j + h;
-            const f32x4 v =
-                *reinterpret_cast<const f32x4 *>(&region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
-            const int row = row0 + 32 * i + r;
-            if (MODE == kPostPartial) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw,
-                                                       (row * ldw + col) * 4, 0, 0);
-                continue;
-            }
-            const uint32_t off =
-                col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
-            f32x4 out;
+                for (int e = 0; e < 4; ++e)
+                    out[e] = alpha * (MODE == kAddPartial ? v[e] + pv[u][e] : v[e]);
+                if (read_c) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                out[e] = alpha * (MODE == kAddPartial ? v[e] + pv[j][e] : v[e]);
-            if (read_c) {
+                    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cv[u][e], out[e]);
+                }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cv[j][e], out[e]);
+                for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], act);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
+                                                       static_cast<int>(off), 0, 0);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
-                                                   static_cast<int>(off), 0, 0);
         }
     }
 }
 
-template <int BM, int BN, bool KTAIL>
+template <int BM, int BN, bool KTAIL, bool EPI>
 __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, int K, float alpha,
                                                                 float beta,
                                                                 const uint16_t *__restrict__ A,
                                                                 const uint16_t *__restrict__ B,
                                                                 float *C, int tiles_m,
-                                                                int tiles_n) {
+                                                                int tiles_n, Epi epi) {
     using T = Tile<BM, BN>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][T::A_STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][T::B_STAGE];
@@ -533,7 +557,8 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
-    store_c_tile<T::MI, T::NI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta);
+    store_c_tile<T::MI, T::NI, EPI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta,
+                                    epi.bias ? epi.bias + n0 : nullptr, epi.act);
 }
 
 // ---------------------------------------------------------------------------
@@ -597,13 +622,13 @@ __device__ __forceinline__ int swz_a32(int r) { return (r >> 2) & 3; }
 // lgkmcnt 11:8 left at their maxima).
 constexpr int wait_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
 
-template <int BM, int BN, int S, bool KTAIL>
+template <int BM, int BN, int S, bool KTAIL, bool EPI>
 __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, float alpha,
                                                          float beta,
                                                          const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, float *C,
                                                          int tiles_m, int tiles_n,
-                                                         PPSplit split_plan) {
+                                                         PPSplit split_plan, Epi epi) {
     using T = PPTile<BM, BN>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][T::A_STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][T::B_STAGE];
@@ -802,9 +827,10 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     float *region = wave < 4 ? reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096
                              : reinterpret_cast<float *>(&lds_b[0][0]) + (wave - 4) * 4096;
     const int row0 = wm * T::WM, col0 = wn * T::WN;
+    const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
     if (split < 0) {
-        store_c_tile_lds<T::MI, T::NI, kStoreC>(acc, region, rc, row0, col0, N - n0, N, alpha,
-                                                beta, rc, 0);
+        store_c_tile_lds<T::MI, T::NI, kStoreC, kSystemScope, EPI>(
+            acc, region, rc, row0, col0, N - n0, N, alpha, beta, rc, 0, bias, epi.act);
         return;
     }
     // A split tile: its partial lives in the workspace slot of the pair.
@@ -852,11 +878,11 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     __syncthreads();
     const float a = s_ready ? alpha : __builtin_nanf("");
     if (local)
-        store_c_tile_lds<T::MI, T::NI, kAddPartial, kDeviceScope>(acc, region, rc, row0, col0,
-                                                                  N - n0, N, a, beta, rw, BN);
+        store_c_tile_lds<T::MI, T::NI, kAddPartial, kDeviceScope, EPI>(
+            acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
     else
-        store_c_tile_lds<T::MI, T::NI, kAddPartial>(acc, region, rc, row0, col0, N - n0, N, a,
-                                                    beta, rw, BN);
+        store_c_tile_lds<T::MI, T::NI, kAddPartial, kSystemScope, EPI>(
+            acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
 }
 
 // ---------------------------------------------------------------------------
@@ -888,13 +914,13 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
 // (a K tail) are skipped per step.  The epilogue stages each wave's tile
 // through LDS (store_c_tile_lds128), about 1 % faster than direct 16-byte
 // stores.
-template <bool KTAIL>
+template <bool KTAIL, bool EPI>
 __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, float alpha,
                                                          float beta,
                                                          const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, float *C,
                                                          int tiles_m, int tiles_n,
-                                                         PPSplit split_plan) {
+                                                         PPSplit split_plan, Epi epi) {
     constexpr int BM = 256, BN = 256, S = 4, BK = kPPBK;
     constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
@@ -1094,8 +1120,10 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     static_assert(S * A_STAGE * 2 >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
     const int row0 = wm * WM, col0 = wn * WN;
+    const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
     if (split < 0) {
-        store_c_tile_lds128<MI>(acc, region, rc, row0, col0, N - n0, N, alpha, beta, rc, 0);
+        store_c_tile_lds128<MI, kStoreC, kSystemScope, EPI>(acc, region, rc, row0, col0, N - n0,
+                                                            N, alpha, beta, rc, 0, bias, epi.act);
         return;
     }
     // A split tile: the partial lives in the workspace slot of the pair; the
@@ -1138,11 +1166,11 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     __syncthreads();
     const float a = s_ready ? alpha : __builtin_nanf("");
     if (local)
-        store_c_tile_lds128<MI, kAddPartial, kDeviceScope>(acc, region, rc, row0, col0, N - n0,
-                                                           N, a, beta, rw, BN);
+        store_c_tile_lds128<MI, kAddPartial, kDeviceScope, EPI>(
+            acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
     else
-        store_c_tile_lds128<MI, kAddPartial>(acc, region, rc, row0, col0, N - n0, N, a, beta,
-                                             rw, BN);
+        store_c_tile_lds128<MI, kAddPartial, kSystemScope, EPI>(
+            acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
 }
 
 
@@ -1167,78 +1195,84 @@ int tile_lds_bytes(int c) {
     return (c == 0 || c == 4) ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
 }
 
+// Calls f(ktail, epi) with the two flags as std::integral_constant values, so
+// that a launcher can pick one of its four kernel instantiations.
+template <class F>
+void with_flags(bool ktail, bool epi, F &&f) {
+    if (ktail) {
+        if (epi) f(std::true_type(), std::true_type());
+        else f(std::true_type(), std::false_type());
+    } else {
+        if (epi) f(std::false_type(), std::true_type());
+        else f(std::false_type(), std::false_type());
+    }
+}
+
+// Checks a split plan against the tile count and K; fills `plan` (whole
+// tiles only when split is null).
+bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan) {
+    plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
+    if (split == nullptr) return true;
+    const int steps = (K + kPPBK - 1) / kPPBK;
+    if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
+        split->split_step >= steps ||
+        (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
+        (split->xcd_pairs && (tiles - split->split_from) % 8 != 0))
+        return false;
+    plan = *split;
+    plan.grid_tiles = static_cast<int>(tiles);
+    return true;
+}
+
 hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                     const uint16_t *B, float *C, const PPSplit *split, hipStream_t stream) {
+                     const uint16_t *B, float *C, const PPSplit *split, const Epi &epi,
+                     hipStream_t stream) {
     const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x3fffffffLL) return hipErrorInvalidValue;
-    PPSplit plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
-    if (split != nullptr) {
-        const int steps = (K + kPPBK - 1) / kPPBK;
-        if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
-            split->split_step >= steps ||
-            (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
-            (split->xcd_pairs && (tiles - split->split_from) % 8 != 0))
-            return hipErrorInvalidValue;
-        plan = *split;
-        plan.grid_tiles = static_cast<int>(tiles);
-    }
+    PPSplit plan;
+    if (!make_plan(split, tiles, K, plan)) return hipErrorInvalidValue;
     const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
-    const dim3 block(kThreads);
-    if (K % kPPBK == 0)
-        bf16_q4_kernel<false><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
-            plan);
-    else
-        bf16_q4_kernel<true><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
-            plan);
+    with_flags(K % kPPBK != 0, epi_on(epi), [&](auto ktail, auto e) {
+        bf16_q4_kernel<decltype(ktail)::value, decltype(e)::value>
+            <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
+                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
+                static_cast<int>(tiles_n), plan, epi);
+    });
     return hipGetLastError();
 }
 
 template <int BM, int BN>
 hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                      const uint16_t *B, float *C, hipStream_t stream) {
+                      const uint16_t *B, float *C, const Epi &epi, hipStream_t stream) {
     const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
-    if (K % kBK == 0)
-        bf16_mfma_kernel<BM, BN, false><<<grid, block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
-    else
-        bf16_mfma_kernel<BM, BN, true><<<grid, block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+    with_flags(K % kBK != 0, epi_on(epi), [&](auto ktail, auto e) {
+        bf16_mfma_kernel<BM, BN, decltype(ktail)::value, decltype(e)::value>
+            <<<dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream>>>(
+                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
+                static_cast<int>(tiles_n), epi);
+    });
     return hipGetLastError();
 }
 
 template <int BM, int BN, int S>
 hipError_t launch_pp(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                     const uint16_t *B, float *C, const PPSplit *split, hipStream_t stream) {
+                     const uint16_t *B, float *C, const PPSplit *split, const Epi &epi,
+                     hipStream_t stream) {
     const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x3fffffffLL) return hipErrorInvalidValue;
-    PPSplit plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
-    if (split != nullptr) {
-        const int steps = (K + kPPBK - 1) / kPPBK;
-        if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
-            split->split_step >= steps ||
-            (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
-            (split->xcd_pairs && (tiles - split->split_from) % 8 != 0))
-            return hipErrorInvalidValue;
-        plan = *split;
-        plan.grid_tiles = static_cast<int>(tiles);
-    }
+    PPSplit plan;
+    if (!make_plan(split, tiles, K, plan)) return hipErrorInvalidValue;
     const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
-    const dim3 block(512);
-    if (K % kPPBK == 0)
-        bf16_pp_kernel<BM, BN, S, false><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
-            plan);
-    else
-        bf16_pp_kernel<BM, BN, S, true><<<dim3(static_cast<unsigned>(grid)), block, 0, stream>>>(
-            M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
-            plan);
+    with_flags(K % kPPBK != 0, epi_on(epi), [&](auto ktail, auto e) {
+        bf16_pp_kernel<BM, BN, S, decltype(ktail)::value, decltype(e)::value>
+            <<<dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream>>>(
+                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
+                static_cast<int>(tiles_n), plan, epi);
+    });
     return hipGetLastError();
 }
 
@@ -1293,14 +1327,16 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
 
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
-                            hipStream_t stream) {
+                            const Epi &epi, hipStream_t stream) {
     if (split != nullptr && !bf16_config_splits(cfg)) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return launch_q4(M, N, K, alpha, beta, A, B, C, split, stream);
-        case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, stream);
-        case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, stream);
-        case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, stream);
-        case 4: return launch_pp<kPPTile, kPPTile, 4>(M, N, K, alpha, beta, A, B, C, split, stream);
+        case 0: return launch_q4(M, N, K, alpha, beta, A, B, C, split, epi, stream);
+        case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, epi, stream);
+        case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, epi, stream);
+        case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, epi, stream);
+        case 4:
+            return launch_pp<kPPTile, kPPTile, 4>(M, N, K, alpha, beta, A, B, C, split, epi,
+                                                  stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace mgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -18,6 +20,39 @@ constexpr int kNumXcd = 8;
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// ---- fused Linear-layer epilogue: y = act(x + bias[col]) ------------------
+// x is alpha * acc (+ beta * C) in fp32; GELU is x * Phi(x) with Phi written
+// through erfc (no 1 + erf cancellation for negative x), SiLU x / (1 + e^-x).
+__device__ __forceinline__ float activate(float x, int act) {
+    switch (act) {
+        case kActRelu: return x < 0.0f ? 0.0f : x;
+        case kActGelu: return 0.5f * x * erfcf(-0.70710678118654752f * x);
+        case kActSilu: return x / (1.0f + expf(-x));
+        default: return x;
+    }
+}
+// The bias of columns col .. col + 3 (bias points at column 0 of the range
+// the caller addresses; zero at or past `cols` or without a bias).
+template <bool EPI>
+__device__ __forceinline__ f32x4 bias4(const float *bias, int col, int cols) {
+    f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI) {
+        if (bias != nullptr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (col + e < cols) b[e] = bias[col + e];
+        }
+    }
+    return b;
+}
+template <bool EPI>
+__device__ __forceinline__ float epi_apply(float x, float b, int act) {
+    if constexpr (EPI)
+        return activate(x + b, act);
+    else
+        return x;
 }
 
 // Pack the low halves / high halves of two dwords: lo16(x) | lo16(y) << 16

@@ -68,13 +68,13 @@ __device__ __forceinline__ f32x4 load4(const float *__restrict__ base, size_t ro
     return v;
 }
 
-template <bool VEC>
+template <bool VEC, bool EPI>
 __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int K, float alpha,
                                                                float beta,
                                                                const float *__restrict__ A,
                                                                const float *__restrict__ B,
                                                                float *C, int tiles_m,
-                                                               int tiles_n) {
+                                                               int tiles_n, Epi epi) {
     __shared__ __attribute__((aligned(16))) float As[2][kBM][kLdA];
     __shared__ __attribute__((aligned(16))) float Bs[2][kBK][kLdB];
 
@@ -198,6 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
                 const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * h;
                 if (row >= M) continue;
                 float *c = C + static_cast<size_t>(row) * N + col;
+                const f32x4 bv = bias4<EPI>(epi.bias, col, N);
                 if (VEC) {
                     if (col >= N) continue;
                     f32x4 out;
@@ -207,6 +208,8 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
 #pragma unroll
                         for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[i][j][g][e], out[e]);
                     }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], epi.act);
                     *reinterpret_cast<f32x4 *>(c) = out;
                 } else {
 #pragma unroll
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
                         if (col + e < N) {
                             float out = alpha * acc[i][j][4 * g + e];
                             if (beta != 0.0f) out = fmaf(beta, c[e], out);
-                            c[e] = out;
+                            c[e] = epi_apply<EPI>(out, bv[e], epi.act);
                         }
                     }
                 }
@@ -249,11 +252,13 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
 __device__ __forceinline__ int swz_fa(int m) { return (m >> 1) & 7; }
 __device__ __forceinline__ int swz_fb(int k) { return ((k >> 4) & 1) << 3; }
 
+template <bool EPI>
 __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int K, float alpha,
                                                              float beta,
                                                              const float *__restrict__ A,
                                                              const float *__restrict__ B,
-                                                             float *C, int tiles_m, int tiles_n) {
+                                                             float *C, int tiles_m, int tiles_n,
+                                                             Epi epi) {
     __shared__ __attribute__((aligned(16))) float As[2][kBM * kBK];
     __shared__ __attribute__((aligned(16))) float Bs[2][kBK * kBN];
 
@@ -400,6 +405,9 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[i][g][half][e], out[e]);
                 }
+                const f32x4 bv = bias4<EPI>(epi.bias, col, N);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], epi.act);
                 *reinterpret_cast<f32x4 *>(c) = out;
             }
         }
@@ -412,25 +420,31 @@ const char *f32_mfma_name(bool vec) {
     return vec ? "f32_mfma_128x128x32_vec4" : "f32_mfma_128x128x32_scalar";
 }
 
-hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const float *A,
-                           const float *B, float *C, bool vec, hipStream_t stream) {
+template <bool EPI>
+hipError_t launch_f32(int M, int N, int K, float alpha, float beta, const float *A,
+                      const float *B, float *C, bool vec, const Epi &epi, hipStream_t stream) {
     const long long tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
     if (vec && K < (1 << 21) && N < (1 << 22))
-        f32_dma_kernel<<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                  static_cast<int>(tiles_m),
-                                                  static_cast<int>(tiles_n));
+        f32_dma_kernel<EPI><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn,
+                                                        epi);
     else if (vec)
-        f32_mfma_kernel<true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                          static_cast<int>(tiles_m),
-                                                          static_cast<int>(tiles_n));
+        f32_mfma_kernel<true, EPI><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                               tm, tn, epi);
     else
-        f32_mfma_kernel<false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                           static_cast<int>(tiles_m),
-                                                           static_cast<int>(tiles_n));
+        f32_mfma_kernel<false, EPI><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                                tm, tn, epi);
     return hipGetLastError();
+}
+
+hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const float *A,
+                           const float *B, float *C, bool vec, const Epi &epi,
+                           hipStream_t stream) {
+    return epi_on(epi) ? launch_f32<true>(M, N, K, alpha, beta, A, B, C, vec, epi, stream)
+                       : launch_f32<false>(M, N, K, alpha, beta, A, B, C, vec, epi, stream);
 }
 
 }  // namespace mgemm

@@ -8,14 +8,28 @@
 
 namespace mgemm {
 
+// Fused Linear-layer epilogue, applied after alpha and beta:
+// C = act(alpha * A * B + beta * C + bias[n]).  Every launcher takes one;
+// {nullptr, kActNone} is the plain GEMM, and kernels are instantiated without
+// the epilogue code for it.
+enum Activation { kActNone = 0, kActRelu = 1, kActGelu = 2, kActSilu = 3 };
+struct Epi {
+    const float *bias;  // N fp32 values in device memory, or nullptr
+    int act;            // an Activation
+};
+inline bool epi_on(const Epi &e) { return e.bias != nullptr || e.act != kActNone; }
+constexpr Epi kNoEpi = {nullptr, kActNone};
+
 // One thread per output element (the unoptimised starting point).
 hipError_t launch_naive_f32(int M, int N, int K, float alpha, float beta, const float *A,
-                            const float *B, float *C, hipStream_t stream);
+                            const float *B, float *C, const Epi &epi, hipStream_t stream);
 hipError_t launch_naive_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                             const uint16_t *B, float *C, hipStream_t stream);
+                             const uint16_t *B, float *C, const Epi &epi, hipStream_t stream);
 
-// C = beta * C (zeros when beta == 0): the K == 0 case.
-hipError_t launch_scale_c(int M, int N, float beta, float *C, hipStream_t stream);
+// C = act(beta * C + bias) (beta * C, or zeros when beta == 0, without an
+// epilogue): the K == 0 case.
+hipError_t launch_scale_c(int M, int N, float beta, float *C, const Epi &epi,
+                          hipStream_t stream);
 
 // Fill `count` ints with zero (workspace counters).
 hipError_t launch_zero_ints(int *p, int count, hipStream_t stream);
@@ -23,7 +37,8 @@ hipError_t launch_zero_ints(int *p, int count, hipStream_t stream);
 // fp32 LDS-tiled fp32-MFMA kernel.  `vec` selects 16-byte accesses, which
 // need K % 4 == 0, N % 4 == 0 and 16-byte aligned A, B and C.
 hipError_t launch_f32_mfma(int M, int N, int K, float alpha, float beta, const float *A,
-                           const float *B, float *C, bool vec, hipStream_t stream);
+                           const float *B, float *C, bool vec, const Epi &epi,
+                           hipStream_t stream);
 const char *f32_mfma_name(bool vec);
 
 // bf16 LDS-tiled MFMA kernel.  Needs K % 8 == 0, N % 8 == 0, 16-byte
@@ -64,7 +79,7 @@ bool bf16_config_splits(int cfg);  // the 256 x 256 kernels, which can split a l
 int bf16_pp_split_tiles(int M, int N, int K, int num_cus);    // 0: no split
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
-                            hipStream_t stream);
+                            const Epi &epi, hipStream_t stream);
 
 // Skinny-M (M <= 16) bf16 kernel that streams B once from HBM.  Needs
 // K % 8 == 0, N % 8 == 0 and 16-byte aligned A, B and C.  With splits > 1 the
@@ -82,7 +97,8 @@ int skinny_pick_splits(int M, int N, int K, int num_cus, bool xcd_local);
 bool skinny_slice_fits(int M, int N, int K, int splits);
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
-                              int *counters, int counter_ints, hipStream_t stream);
+                              int *counters, int counter_ints, const Epi &epi,
+                              hipStream_t stream);
 
 // Split-K skinny kernel with most of its reduction kept inside XCDs.  On a
 // device that deals workgroups to its eight XCDs in round-robin order, so
@@ -102,7 +118,8 @@ bool skinny_xcd_local_fits(int M, int N, int K, int splits);
 hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
                                   const uint16_t *A, const uint16_t *B, float *C, int splits,
                                   float *partials, int *counters, int counter_ints,
-                                  char *xcd_base, int xcd_group, hipStream_t stream);
+                                  char *xcd_base, int xcd_group, const Epi &epi,
+                                  hipStream_t stream);
 // Runs a probe grid on `stream`, waits for it, and sets *ok when every
 // workgroups whose ids are equal modulo kXcdCount ran on one XCD and the
 // kXcdCount residues on different XCDs (which XCD takes workgroup 0 varies

@@ -5,7 +5,8 @@
 // wavefront's B reads are contiguous (section 10.3.2 explains why the other
 // mapping is several times slower); blocks are 16 x 16 threads.  Unlike the
 // page's listing this one applies the full alpha/beta update, accepts bf16
-// inputs, and flattens the grid to one dimension.  Its per-thread arithmetic
+// inputs, flattens the grid to one dimension and can apply the fused
+// bias / activation epilogue.  Its per-thread arithmetic
 // intensity is 2K / (8K + 4), about 1/4 FLOP per byte, so it is left far
 // below the roofline on purpose.
 #include "common.h"
@@ -20,11 +21,11 @@ __device__ __forceinline__ float load_elem(const uint16_t *p, size_t i) {
     return bf16_bits_to_float(p[i]);
 }
 
-template <typename T>
+template <typename T, bool EPI>
 __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float alpha, float beta,
                                                     const T *__restrict__ A,
                                                     const T *__restrict__ B, float *C,
-                                                    int tiles_n) {
+                                                    int tiles_n, Epi epi) {
     const int tile = blockIdx.x;
     const int row = (tile / tiles_n) * 16 + threadIdx.y;
     const int col = (tile % tiles_n) * 16 + threadIdx.x;
@@ -36,13 +37,17 @@ __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float a
     const size_t idx = static_cast<size_t>(row) * N + col;
     float out = alpha * sum;
     if (beta != 0.0f) out = fmaf(beta, C[idx], out);
-    C[idx] = out;
+    C[idx] = epi_apply<EPI>(out, EPI && epi.bias ? epi.bias[col] : 0.0f, epi.act);
 }
 
-__global__ __launch_bounds__(256) void scale_kernel(size_t count, float beta, float *C) {
+template <bool EPI>
+__global__ __launch_bounds__(256) void scale_kernel(size_t count, int N, float beta, float *C,
+                                                    Epi epi) {
     const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride)
-        C[i] = (beta != 0.0f) ? beta * C[i] : 0.0f;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) {
+        const float v = (beta != 0.0f) ? beta * C[i] : 0.0f;
+        C[i] = epi_apply<EPI>(v, EPI && epi.bias ? epi.bias[i % N] : 0.0f, epi.act);
+    }
 }
 
 __global__ __launch_bounds__(256) void zero_ints_kernel(int *p, int count) {
@@ -52,32 +57,42 @@ __global__ __launch_bounds__(256) void zero_ints_kernel(int *p, int count) {
 
 template <typename T>
 hipError_t launch_naive(int M, int N, int K, float alpha, float beta, const T *A, const T *B,
-                        float *C, hipStream_t stream) {
+                        float *C, const Epi &epi, hipStream_t stream) {
     const long long tiles_m = (M + 15) / 16, tiles_n = (N + 15) / 16;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    naive_kernel<T><<<dim3(static_cast<unsigned>(tiles)), dim3(16, 16), 0, stream>>>(
-        M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_n));
+    const dim3 grid(static_cast<unsigned>(tiles)), block(16, 16);
+    if (epi_on(epi))
+        naive_kernel<T, true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                          static_cast<int>(tiles_n), epi);
+    else
+        naive_kernel<T, false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                           static_cast<int>(tiles_n), epi);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_naive_f32(int M, int N, int K, float alpha, float beta, const float *A,
-                            const float *B, float *C, hipStream_t stream) {
-    return launch_naive<float>(M, N, K, alpha, beta, A, B, C, stream);
+                            const float *B, float *C, const Epi &epi, hipStream_t stream) {
+    return launch_naive<float>(M, N, K, alpha, beta, A, B, C, epi, stream);
 }
 
 hipError_t launch_naive_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                             const uint16_t *B, float *C, hipStream_t stream) {
-    return launch_naive<uint16_t>(M, N, K, alpha, beta, A, B, C, stream);
+                             const uint16_t *B, float *C, const Epi &epi, hipStream_t stream) {
+    return launch_naive<uint16_t>(M, N, K, alpha, beta, A, B, C, epi, stream);
 }
 
-hipError_t launch_scale_c(int M, int N, float beta, float *C, hipStream_t stream) {
+hipError_t launch_scale_c(int M, int N, float beta, float *C, const Epi &epi,
+                          hipStream_t stream) {
     const size_t count = static_cast<size_t>(M) * N;
     size_t blocks = (count + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    scale_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(count, beta, C);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (epi_on(epi))
+        scale_kernel<true><<<grid, block, 0, stream>>>(count, N, beta, C, epi);
+    else
+        scale_kernel<false><<<grid, block, 0, stream>>>(count, N, beta, C, epi);
     return hipGetLastError();
 }
 

@@ -106,7 +106,7 @@ struct Stage {
 // scratch block at xcd_base + x * kSkinnyXcdBytes (counters first, then the partials
 // of its column blocks, 128 columns wide), so that part of the reduction
 // stays in one XCD's L2.  Every XCD gets the same number of workgroups.
-template <bool XCD_LOCAL>
+template <bool XCD_LOCAL, bool EPI>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, float alpha,
                                                           float beta,
                                                           const uint16_t *__restrict__ A,
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
                                                           float *C, int splits, int kblk_per_split,
                                                           float *partials, int *counters,
                                                           int counter_stride, char *xcd_base,
-                                                          int xcd_group) {
+                                                          int xcd_group, Epi epi) {
     __shared__ f32x4 red[kWaves][8][64];
     __shared__ int s_last;
 
@@ -270,6 +270,14 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
                 o1[t] = fmaf(beta, c1[t], o1[t]);
             }
         }
+        if constexpr (EPI) {
+            const f32x4 b0 = bias4<EPI>(epi.bias, nn, N), b1 = bias4<EPI>(epi.bias, nn + 4, N);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                o0[t] = epi_apply<EPI>(o0[t], b0[t], epi.act);
+                o1[t] = epi_apply<EPI>(o1[t], b1[t], epi.act);
+            }
+        }
         reinterpret_cast<f32x4 *>(c)[0] = o0;
         reinterpret_cast<f32x4 *>(c)[1] = o1;
     };
@@ -376,7 +384,8 @@ bool skinny_slice_fits(int M, int N, int K, int splits) {
 
 hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                               const uint16_t *B, float *C, int splits, float *partials,
-                              int *counters, int counter_ints, hipStream_t stream) {
+                              int *counters, int counter_ints, const Epi &epi,
+                              hipStream_t stream) {
     if (M < 1 || M > kSkinnyMaxM || splits < 1) return hipErrorInvalidValue;
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
@@ -393,9 +402,15 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const int counter_stride = col_blocks * kCounterLine <= counter_ints ? kCounterLine : 1;
     if (real_splits > 1 && col_blocks > counter_ints) return hipErrorInvalidValue;
-    skinny_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
-        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters, counter_stride,
-        nullptr, 1);
+    const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
+    if (epi_on(epi))
+        skinny_kernel<false, true><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                          real_splits, per, partials, counters,
+                                                          counter_stride, nullptr, 1, epi);
+    else
+        skinny_kernel<false, false><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                           real_splits, per, partials, counters,
+                                                           counter_stride, nullptr, 1, epi);
     return hipGetLastError();
 }
 
@@ -465,7 +480,8 @@ bool skinny_xcd_local_fits(int M, int N, int K, int splits) {
 hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
                                   const uint16_t *A, const uint16_t *B, float *C, int splits,
                                   float *partials, int *counters, int counter_ints,
-                                  char *xcd_base, int xcd_group, hipStream_t stream) {
+                                  char *xcd_base, int xcd_group, const Epi &epi,
+                                  hipStream_t stream) {
     if (xcd_base == nullptr || !skinny_xcd_local_fits(M, N, K, splits)) return hipErrorInvalidValue;
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
@@ -483,9 +499,16 @@ hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
     const long long grid =
         rest_groups + static_cast<long long>(col_blocks - rest) * real_splits;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    skinny_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
-        M, N, K, alpha, beta, A, B, C, real_splits, per, partials, counters, counter_stride,
-        xcd_base, xcd_group < 1 ? 1 : xcd_group);
+    const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
+    const int grp = xcd_group < 1 ? 1 : xcd_group;
+    if (epi_on(epi))
+        skinny_kernel<true, true><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                         real_splits, per, partials, counters,
+                                                         counter_stride, xcd_base, grp, epi);
+    else
+        skinny_kernel<true, false><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                          real_splits, per, partials, counters,
+                                                          counter_stride, xcd_base, grp, epi);
     return hipGetLastError();
 }
 

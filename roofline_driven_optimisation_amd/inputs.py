@@ -107,6 +107,12 @@ def make_case(M: int, N: int, K: int, dtype: str = "f32", alpha: float = 1.0,
                 float(alpha), float(beta), A, B, C, seed)
 
 
+def make_bias(N: int, dist: str = "n:0.5", seed: int = 0) -> np.ndarray:
+    """A seeded float32 bias vector over N output columns (its own generator,
+    seeded apart from the operands')."""
+    return _draw(np.random.default_rng([seed, 0xB1A5]), (N,), dist)
+
+
 @dataclass(frozen=True)
 class Workload:
     """A named shape with its distributions, alpha and beta."""
