@@ -46,7 +46,11 @@ from roofline_driven_optimisation_amd.inputs import workload  # noqa: E402
 HEADLINE = "bf16_4096"
 SECONDARY = ["f32_4096", "f32_4092", "prefill_qkv", "prefill_o", "prefill_gate_up",
              "prefill_down", "decode_up_m1", "decode_up_m8", "decode_up_m16",
-             "decode_down_m1", "decode_down_m8", "decode_down_m16", "decode_lm_head"]
+             "decode_down_m1", "decode_down_m8", "decode_down_m16", "decode_lm_head",
+             "prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu"]
+# "<workload>+bias_<act>": the workload through the fused Linear-layer
+# epilogue, C = act(A*B + bias) with a normal(0, 0.5) bias over the columns
+ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 ROTATE_BYTES = 2 * 256 * 2 ** 20  # twice the MI355X Infinity Cache
 
 
@@ -84,7 +88,16 @@ class Prepared:
 
     def __init__(self, name: str, seed: int = 0):
         import torch
-        self.w = workload(name)
+        from roofline_driven_optimisation_amd.inputs import make_bias
+        base, _, epi = name.partition("+")
+        self.name = name
+        self.w = workload(base)
+        self.epi = None
+        if epi:
+            if not epi.startswith("bias_") or epi[5:] not in ACTIVATIONS:
+                raise ValueError("unknown epilogue %r" % epi)
+            bias = torch.from_numpy(make_bias(self.w.N, "n:0.5", seed)).cuda()
+            self.epi = (bias, ACTIVATIONS[epi[5:]])
         case = self.w.case(seed)
         self.case = case
         if case.bf16:
@@ -101,7 +114,8 @@ class Prepared:
         A, B, C = A.cuda(), B.cuda(), C.cuda()
         self.bufs = [(A, B, C)] + [(A.clone(), B.clone(), C.clone()) for _ in range(self.sets - 1)]
         self.C0 = C.clone() if case.C is not None else None
-        self.rf = rl.gemm_roofline(case.M, case.N, case.K, case.dtype, case.beta != 0.0)
+        self.rf = rl.gemm_roofline(case.M, case.N, case.K, case.dtype, case.beta != 0.0,
+                                   bias=self.epi is not None)
 
     def launch(self, i: int, naive: bool = False):
         from roofline_driven_optimisation_amd import binding
@@ -109,6 +123,9 @@ class Prepared:
         if naive:
             fn = binding.gemm_naive_bf16 if self.case.bf16 else binding.gemm_naive_f32
             fn(A, B, C, self.w.alpha, self.w.beta)
+        elif self.epi is not None:
+            fn = binding.gemm_bf16_bias_act if self.case.bf16 else binding.gemm_f32_bias_act
+            fn(A, B, C, self.epi[0], self.epi[1], self.w.alpha, self.w.beta)
         else:
             binding.gemm(A, B, C, self.w.alpha, self.w.beta)
 
@@ -155,7 +172,7 @@ def summary(p: Prepared, sec: float, kname: str) -> dict:
     tflops = p.rf.flops / sec / 1e12
     gbs = p.rf.nbytes / sec / 1e9
     return {
-        "workload": p.w.name, "M": p.w.M, "N": p.w.N, "K": p.w.K, "dtype": p.w.dtype,
+        "workload": p.name, "M": p.w.M, "N": p.w.N, "K": p.w.K, "dtype": p.w.dtype,
         "alpha": p.w.alpha, "beta": p.w.beta, "kernel": kname, "us": round(sec * 1e6, 2),
         "tflops": round(tflops, 2), "gbs": round(gbs, 1), "bound": p.rf.bound,
         "roofline_tflops": round(p.rf.attainable / 1e12, 1),
@@ -391,6 +408,14 @@ def main():
         also.append(s)
         del p
         torch.cuda.empty_cache()
+
+    # fused-epilogue entries: the plain GEMM of the same shape beside them
+    plain = {s_["workload"]: s_["us"] for s_ in also}
+    for s_ in also:
+        base = s_["workload"].partition("+")[0]
+        if base != s_["workload"] and base in plain:
+            s_["plain_us"] = plain[base]
+            s_["epilogue_us"] = round(s_["us"] - plain[base], 2)
 
     floor = launch_floor()
     log("bench: launch floor " + json.dumps(floor))

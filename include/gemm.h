@@ -117,8 +117,11 @@ GEMM_API int gemm_bf16(int M, int N, int K, float alpha, float beta,
  *               GEMM_ACT_NONE  x;
  *               GEMM_ACT_RELU  0 for x < 0, else x (NaN stays NaN);
  *               GEMM_ACT_GELU  x * Phi(x), Phi the standard normal CDF
- *                              (the erf form, computed through erfcf);
- *               GEMM_ACT_SILU  x / (1 + exp(-x)).
+ *                              (the erf form; Phi from the erf
+ *                              approximation 7.1.26 of Abramowitz and
+ *                              Stegun, absolute error <= 1.5e-7);
+ *               GEMM_ACT_SILU  x / (1 + exp(-x)) (hardware exponential and
+ *                              reciprocal).
  *               Any other value returns GEMM_ERR_INVALID_ARG and launches
  *               nothing.
  * With K == 0 the result is act(beta * C + bias) (zeros plus bias when beta

@@ -198,6 +198,9 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
     const bool read_c = beta != 0.0f;
+    // the lane's four columns are the same in both halves: bias loaded once,
+    // before any store
+    const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col0 + 4 * (lane & 15), cols_left);
 #pragma unroll
     for (int half = 0; half < MI / 2; ++half) {
 #pragma unroll
@@ -216,7 +219,6 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
         }
         const int chunk = lane & 15;
         const int col = col0 + 4 * chunk;
-        const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col, cols_left);
         // Rows in groups of kGroup: the group's global loads (partial, C)
         // are all issued before its stores.  The compiler cannot tell the
         // loaded buffers from the stored C apart, so a load placed after a
@@ -291,6 +293,9 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
     const bool read_c = beta != 0.0f;
+    // a lane stores the same four columns in every pass: their bias is
+    // loaded once, before any store (a load after a store to C would wait)
+    const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col0 + 4 * (lane & 31), cols_left);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -305,13 +310,15 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
             }
         const int chunk = lane & 31;
         const int col = col0 + 4 * chunk;
-        const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col, cols_left);
         // The rows' global loads (partial, C) are issued a group at a time
-        // (all 16 rows; 8 with the fused epilogue, whose activation needs
-        // registers of its own) before the group's stores: the compiler
-        // cannot tell the loaded buffers from the stored C apart, so a load
-        // placed after a store would wait for it.
-        constexpr int kGroup = EPI ? 8 : 16;
+        // (all 16 rows) before the group's stores: the compiler cannot tell
+        // the loaded buffers from the stored C apart, so a load placed after
+        // a store would wait for it.
+        // With the fused epilogue the combined values go back to the same
+        // LDS slots, and a rolled loop applies bias and activation and stores
+        // them: one copy of the activation code instead of 64 (fully
+        // unrolled, they made the compiler keep the accumulators in scratch).
+        constexpr int kGroup = 16;
 #pragma unroll
         for (int j0 = 0; j0 < 16; j0 += kGroup) {
             f32x4 pv[kGroup], cv[kGroup];
@@ -333,16 +340,14 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
 #pragma unroll
             for (int u = 0; u < kGroup; ++u) {
                 const int r = 2 * (j0 + u) + h;
-                const f32x4 v =
-                    *reinterpret_cast<const f32x4 *>(&region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
+                f32x4 *slot = reinterpret_cast<f32x4 *>(&region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
+                const f32x4 v = *slot;
                 const int row = row0 + 32 * i + r;
                 if (MODE == kPostPartial) {
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rw,
                                                            (row * ldw + col) * 4, 0, 0);
                     continue;
                 }
-                const uint32_t off =
-                    col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
                 f32x4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -351,11 +356,41 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cv[u][e], out[e]);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], act);
+                if (EPI) {
+                    *slot = out;
+                    continue;
+                }
+                const uint32_t off =
+                    col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rc,
                                                        static_cast<int>(off), 0, 0);
             }
+        }
+        if constexpr (EPI && MODE != kPostPartial) {
+            // four rows per iteration: their LDS reads are in flight together
+            with_activation(act, [&](auto act_tag) {
+                constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll 1
+                for (int j0 = 0; j0 < 16; j0 += 4) {
+                    f32x4 o[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 2 * (j0 + u) + h;
+                        o[u] = *reinterpret_cast<const f32x4 *>(
+                            &region[r * 128 + ((chunk ^ (r & 15)) * 4)]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[u][e] = activate_t<ACT>(o[u][e] + bv[e]);
+                        const int row = row0 + 32 * i + 2 * (j0 + u) + h;
+                        const uint32_t off =
+                            col < cols_left ? static_cast<uint32_t>((row * N + col) * 4) : kOOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[u]), rc,
+                                                               static_cast<int>(off), 0, 0);
+                    }
+                }
+            });
         }
     }
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mgemm {
@@ -23,14 +25,56 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
 }
 
 // ---- fused Linear-layer epilogue: y = act(x + bias[col]) ------------------
-// x is alpha * acc (+ beta * C) in fp32; GELU is x * Phi(x) with Phi written
-// through erfc (no 1 + erf cancellation for negative x), SiLU x / (1 + e^-x).
+// x is alpha * acc (+ beta * C) in fp32.  The activations are written to be
+// short, because a kernel applies them to every output element:
+//   * GELU, x * Phi(x): Phi from the rational approximation of erf in
+//     Abramowitz and Stegun, Handbook of Mathematical Functions, formula
+//     7.1.26 (|error| <= 1.5e-7 in erf), used in its complementary form
+//     (0.5 erfc(|x| / sqrt 2) = Phi(-|x|)) so that negative x suffers no
+//     cancellation; an error e in Phi moves the output by |x| e;
+//   * SiLU, x / (1 + e^-x), with the hardware base-2 exponential and
+//     reciprocal (relative errors of a few 1e-7, growing with |x| through
+//     the rounding of -x log2(e));
+//   * ReLU, 0 for x < 0 (NaN passes through).
+__device__ __forceinline__ float phi_neg_abs(float x) {  // Phi(-|x|)
+    const float y = fabsf(x) * 0.70710678118654752f;      // |x| / sqrt 2
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, y, 1.0f));
+    float p = fmaf(1.061405429f, t, -1.453152027f);
+    p = fmaf(p, t, 1.421413741f);
+    p = fmaf(p, t, -0.284496736f);
+    p = fmaf(p, t, 0.254829592f);
+    return 0.5f * (p * t) * __expf(-y * y);
+}
+template <int ACT>
+__device__ __forceinline__ float activate_t(float x) {
+    if constexpr (ACT == kActRelu) {
+        return x < 0.0f ? 0.0f : x;
+    } else if constexpr (ACT == kActGelu) {
+        const float q = phi_neg_abs(x);
+        return x * (x < 0.0f ? q : 1.0f - q);
+    } else if constexpr (ACT == kActSilu) {
+        return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+    } else {
+        return x;
+    }
+}
 __device__ __forceinline__ float activate(float x, int act) {
     switch (act) {
-        case kActRelu: return x < 0.0f ? 0.0f : x;
-        case kActGelu: return 0.5f * x * erfcf(-0.70710678118654752f * x);
-        case kActSilu: return x / (1.0f + expf(-x));
+        case kActRelu: return activate_t<kActRelu>(x);
+        case kActGelu: return activate_t<kActGelu>(x);
+        case kActSilu: return activate_t<kActSilu>(x);
         default: return x;
+    }
+}
+// Calls f(std::integral_constant<int, act>()), so that a loop can be compiled
+// once per activation instead of switching per element.
+template <class F>
+__device__ __forceinline__ void with_activation(int act, F &&f) {
+    switch (act) {
+        case kActRelu: f(std::integral_constant<int, kActRelu>()); break;
+        case kActGelu: f(std::integral_constant<int, kActGelu>()); break;
+        case kActSilu: f(std::integral_constant<int, kActSilu>()); break;
+        default: f(std::integral_constant<int, kActNone>()); break;
     }
 }
 // The bias of columns col .. col + 3 (bias points at column 0 of the range

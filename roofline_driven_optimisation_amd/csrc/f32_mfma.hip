@@ -173,6 +173,14 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
     // With VEC and beta != 0 every C load is issued before the first store
     // (a load the compiler placed after a store to C would wait for it).
     f32x4 cin[2][2][4];
+    // the fused epilogue's bias, by (j, g): the same columns for both i, and
+    // loaded before any store for the same reason as C
+    f32x4 bvs[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            bvs[j][g] = bias4<EPI>(epi.bias, n0 + wn * 64 + 32 * j + 8 * g + 4 * h, N);
     if (VEC && beta != 0.0f) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void f32_mfma_kernel(int M, int N, int
                 const int col = n0 + wn * 64 + 32 * j + 8 * g + 4 * h;
                 if (row >= M) continue;
                 float *c = C + static_cast<size_t>(row) * N + col;
-                const f32x4 bv = bias4<EPI>(epi.bias, col, N);
+                const f32x4 bv = bvs[j][g];
                 if (VEC) {
                     if (col >= N) continue;
                     f32x4 out;
@@ -370,6 +378,13 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
     // cannot tell the loads from the stores to C apart, so a load placed
     // after a store would wait for it (one memory round trip per store).
     f32x4 cin[2][4][2];
+    // the fused epilogue's bias, by (g, half), loaded before any store
+    f32x4 bvs[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+            bvs[g][half] = bias4<EPI>(epi.bias, n0 + wn * 64 + 16 * g + 8 * h + 4 * half, N);
     if (beta != 0.0f) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -405,9 +420,9 @@ __global__ __launch_bounds__(kThreads, 2) void f32_dma_kernel(int M, int N, int 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, cin[i][g][half][e], out[e]);
                 }
-                const f32x4 bv = bias4<EPI>(epi.bias, col, N);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = epi_apply<EPI>(out[e], bv[e], epi.act);
+                for (int e = 0; e < 4; ++e)
+                    out[e] = epi_apply<EPI>(out[e], bvs[g][half][e], epi.act);
                 *reinterpret_cast<f32x4 *>(c) = out;
             }
         }

@@ -205,6 +205,16 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
         }
     };
 
+    // The fused epilogue's bias of the block's 128 columns, one per thread,
+    // requested before the stream (one register over the loop) and parked
+    // in LDS for the final store.
+    __shared__ float s_bias[kSkinnyCols];
+    float bias_mine = 0.0f;
+    if constexpr (EPI) {
+        const int nb = cb * kSkinnyCols + tid;
+        if (epi.bias != nullptr && tid < kSkinnyCols && nb < N) bias_mine = epi.bias[nb];
+    }
+
     f32x4 acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -244,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
     // of the block.  Sum the four waves through LDS.
 #pragma unroll
     for (int t = 0; t < 8; ++t) red[wave][t][lane] = acc[t];
+    if (EPI && tid < kSkinnyCols) s_bias[tid] = bias_mine;
     __syncthreads();
 
     const int l = tid & 63, r = tid >> 6;
@@ -271,11 +282,11 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
             }
         }
         if constexpr (EPI) {
-            const f32x4 b0 = bias4<EPI>(epi.bias, nn, N), b1 = bias4<EPI>(epi.bias, nn + 4, N);
+            const int c0 = 8 * (l & 15);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                o0[t] = epi_apply<EPI>(o0[t], b0[t], epi.act);
-                o1[t] = epi_apply<EPI>(o1[t], b1[t], epi.act);
+                o0[t] = epi_apply<EPI>(o0[t], s_bias[c0 + t], epi.act);
+                o1[t] = epi_apply<EPI>(o1[t], s_bias[c0 + 4 + t], epi.act);
             }
         }
         reinterpret_cast<f32x4 *>(c)[0] = o0;

@@ -130,11 +130,15 @@ class Roofline:
         return (self.nbytes / seconds) / self.peak_bw
 
 
-def gemm_roofline(M: int, N: int, K: int, dtype: str, beta_nonzero: bool) -> Roofline:
-    """Roofline position of a GEMM with fp32 output on MI355X."""
+def gemm_roofline(M: int, N: int, K: int, dtype: str, beta_nonzero: bool,
+                  bias: bool = False) -> Roofline:
+    """Roofline position of a GEMM with fp32 output on MI355X.  With ``bias``
+    (the fused Linear-layer epilogue) the N fp32 bias values join the bytes;
+    the epilogue's per-element add and activation are not counted as FLOPs
+    (M N of them against 2 M N K)."""
     in_bytes = ELEM_BYTES[dtype]
     flops = gemm_flops(M, N, K)
-    nbytes = gemm_bytes(M, N, K, in_bytes, 4, beta_nonzero)
+    nbytes = gemm_bytes(M, N, K, in_bytes, 4, beta_nonzero) + (4 * N if bias else 0)
     peak = MI355X_PEAK_BF16 if dtype == "bf16" else MI355X_PEAK_FP32
     ai = flops / nbytes
     att = attainable(peak, MI355X_PEAK_HBM, ai)
