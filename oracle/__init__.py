@@ -63,6 +63,8 @@ class Oracle:
             fn.restype = ctypes.c_int
         lib.oracle_epilogue.argtypes = [i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp]
         lib.oracle_epilogue.restype = ctypes.c_int
+        lib.oracle_sum_f32.argtypes = [i64, vp, vp, vp]
+        lib.oracle_sum_f32.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -169,6 +171,18 @@ class Oracle:
             return self.epilogue(out, den, bias, act, cols=cols)
         return out, den
 
+    def sum_f32(self, x):
+        """fp64 sum of a float32 vector and its sum of magnitudes (the
+        reduction case study of page "Memory hierarchy and cost table",
+        section 4.7): returns (sum, abs_sum)."""
+        x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        out = np.zeros(2, dtype=np.float64)
+        rc = self.lib.oracle_sum_f32(x.size, _ptr(x), out.ctypes.data_as(ctypes.c_void_p),
+                                     ctypes.c_void_p(out.ctypes.data + 8))
+        if rc != 0:
+            raise ValueError("oracle rejected the sum arguments (code %d)" % rc)
+        return float(out[0]), float(out[1])
+
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
@@ -195,6 +209,10 @@ def gemm_entries(A, B, rows, cols, C=None, alpha=1.0, beta=0.0, bf16=False, bias
 
 def epilogue(z, den, bias=None, act=0, cols=None):
     return default().epilogue(z, den, bias, act, cols)
+
+
+def sum_f32(x):
+    return default().sum_f32(x)
 
 
 def num_threads() -> int:

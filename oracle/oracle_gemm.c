@@ -253,6 +253,26 @@ int oracle_epilogue(int64_t count, int64_t N, const int64_t *cols, const double 
     return ORACLE_OK;
 }
 
+/*
+ * Sum of a float32 vector: the memory-bound case study of page "Memory
+ * hierarchy and cost table", section 4.7 (summing 100 million floats).
+ * fp64, ascending index order; beside the sum, the sum of magnitudes
+ * sum |x[i]| that scales the parity tolerance.  n == 0 gives 0 and 0.
+ */
+int oracle_sum_f32(int64_t n, const float *x, double *sum, double *abs_sum)
+{
+    if (n < 0 || sum == NULL || abs_sum == NULL || (n > 0 && x == NULL))
+        return ORACLE_EINVAL;
+    double s = 0.0, a = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        s += (double)x[i];
+        a += fabs((double)x[i]);
+    }
+    *sum = s;
+    *abs_sum = a;
+    return ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int oracle_num_threads(void)
 {

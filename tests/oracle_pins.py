@@ -265,12 +265,43 @@ def pin_epilogue_slope(o):
     assert d[0, 0] == 1.0
 
 
+def pin_sum_closed_forms(o):
+    """Vector sum: Gauss's n (n - 1) / 2 for 0 .. n-1, n for ones, the empty
+    sum, alternating signs, and magnitudes summing to sum |x|."""
+    for n in (1, 2, 7, 1000, 4097):
+        x = np.arange(n, dtype=np.float32)
+        s, a = o.sum_f32(x)
+        assert s == n * (n - 1) / 2 and a == s
+        s, a = o.sum_f32(np.ones(n, np.float32))
+        assert s == n and a == n
+        alt = np.where(np.arange(n) % 2 == 0, 1.0, -1.0).astype(np.float32)
+        s, a = o.sum_f32(alt)
+        assert s == (n % 2) and a == n
+    assert o.sum_f32(np.zeros(0, np.float32)) == (0.0, 0.0)
+
+
+def pin_sum_precision(o):
+    """fp64 accumulation: 1e8 + 1 - 1e8 is 1 (an fp32 accumulator loses the
+    1); random data agrees with math.fsum (exactly rounded) to fp64
+    rounding."""
+    import math
+    s, a = o.sum_f32(np.array([1e8, 1.0, -1e8], dtype=np.float32))
+    assert s == 1.0 and a == 2e8 + 1
+    rng = np.random.default_rng(11)
+    x = rng.uniform(-1, 1, 100003).astype(np.float32)
+    s, a = o.sum_f32(x)
+    ref = math.fsum(x.astype(np.float64))
+    assert abs(s - ref) <= 1e-12 * math.fsum(np.abs(x.astype(np.float64)))
+    assert abs(a - math.fsum(np.abs(x.astype(np.float64)))) <= 1e-12 * a
+
+
 ALL_PINS = [
     pin_hand_signs, pin_rectangular_hand, pin_identity_zero_permutation, pin_all_ones,
     pin_alpha_beta_linearity, pin_transpose_identity, pin_brute_force_integers,
     pin_random_floats_vs_numpy, pin_bf16_widening, pin_beta_zero_reads_no_c, pin_k_zero,
     pin_entries_match_full, pin_entries_hand, pin_den_bounds_result,
     pin_epilogue_closed_forms, pin_epilogue_bias_columns, pin_epilogue_gemm, pin_epilogue_slope,
+    pin_sum_closed_forms, pin_sum_precision,
 ]
 
 
@@ -301,6 +332,10 @@ MUTANTS = {
     "gelu_unscaled_erf": ("erfc(-x / sqrt(2.0))", "erfc(-x)"),
     "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
     "relu_leaky": ("return x < 0.0 ? 0.0 : x;", "return x < 0.0 ? 0.01 * x : x;"),
+    "sum_skips_first": ("for (int64_t i = 0; i < n; ++i) {\n        s += (double)x[i];",
+                        "for (int64_t i = 1; i < n; ++i) {\n        s += (double)x[i];"),
+    "sum_in_float": ("double s = 0.0, a = 0.0;", "float s = 0.0f; double a = 0.0;"),
+    "abs_sum_signed": ("a += fabs((double)x[i]);", "a += (double)x[i];"),
 }
 
 
