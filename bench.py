@@ -47,7 +47,7 @@ HEADLINE = "bf16_4096"
 SECONDARY = ["f32_4096", "f32_4092", "prefill_qkv", "prefill_o", "prefill_gate_up",
              "prefill_down", "decode_up_m1", "decode_up_m8", "decode_up_m16",
              "decode_down_m1", "decode_down_m8", "decode_down_m16", "decode_lm_head",
-             "prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu"]
+             "prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu", "sum_1e8"]
 # "<workload>+bias_<act>": the workload through the fused Linear-layer
 # epilogue, C = act(A*B + bias) with a normal(0, 0.5) bias over the columns
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
@@ -135,6 +135,36 @@ class Prepared:
         return binding.last_kernel()
 
 
+class PreparedSum:
+    """The vector-sum workload "sum_<n>": n float32 values ~ U[-1, 1] (seed
+    0), rotated across copies like the GEMM operands; ``naive`` launches the
+    one-element-per-thread first version."""
+
+    def __init__(self, name: str, seed: int = 0):
+        import torch
+        self.name = name
+        self.n = int(float(name.split("_", 1)[1]))
+        x = np.random.default_rng(seed).uniform(-1.0, 1.0, self.n).astype(np.float32)
+        self.sets = max(1, -(-ROTATE_BYTES // (4 * self.n)))
+        xt = torch.from_numpy(x).cuda()
+        self.bufs = [xt] + [xt.clone() for _ in range(self.sets - 1)]
+        self.out = torch.zeros(1, dtype=torch.float32, device="cuda")
+        self.rf = rl.sum_roofline(self.n)
+
+    def launch(self, i: int, naive: bool = False):
+        from roofline_driven_optimisation_amd import binding
+        binding.reduce_sum_f32(self.bufs[i % self.sets], self.out, naive=naive)
+
+    def kernel_name(self) -> str:
+        from roofline_driven_optimisation_amd import binding
+        self.launch(0)
+        return binding.last_kernel()
+
+
+def prepare(name: str):
+    return PreparedSum(name) if name.startswith("sum_") else Prepared(name)
+
+
 SETTLE_S = 0.1  # minimum untimed warm-up, seconds
 
 
@@ -168,9 +198,13 @@ def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
     return wall, event
 
 
-def summary(p: Prepared, sec: float, kname: str) -> dict:
+def summary(p, sec: float, kname: str) -> dict:
     tflops = p.rf.flops / sec / 1e12
     gbs = p.rf.nbytes / sec / 1e9
+    if isinstance(p, PreparedSum):
+        return {"workload": p.name, "n": p.n, "dtype": "f32", "kernel": kname,
+                "us": round(sec * 1e6, 2), "gbs": round(gbs, 1), "bound": p.rf.bound,
+                "frac": round(p.rf.fraction(sec), 4)}
     return {
         "workload": p.name, "M": p.w.M, "N": p.w.N, "K": p.w.K, "dtype": p.w.dtype,
         "alpha": p.w.alpha, "beta": p.w.beta, "kernel": kname, "us": round(sec * 1e6, 2),
@@ -385,7 +419,7 @@ def main():
 
     if args.only:
         for name in args.only.split(","):
-            p = Prepared(name)
+            p = prepare(name)
             kname = p.kernel_name()
             wall, ev = time_workload(p, args.steps, args.warmup)
             log(json.dumps(summary(p, ev, kname)))
@@ -400,10 +434,15 @@ def main():
     also = []
     for name in SECONDARY:
         log("bench: secondary %s" % name)
-        p = Prepared(name)
+        p = prepare(name)
         kn = p.kernel_name()
         _, sec = time_workload(p, args.secondary_steps, max(3, args.warmup // 4))
         s = summary(p, sec, kn)
+        if isinstance(p, PreparedSum):
+            # the page's first version beside it (the ladder's other rung)
+            _, nsec = time_workload(p, max(3, args.secondary_steps // 4), 3, naive=True)
+            s["naive_us"] = round(nsec * 1e6, 2)
+            s["naive_gbs"] = round(p.rf.nbytes / nsec / 1e9, 1)
         log("  " + json.dumps(s))
         also.append(s)
         del p

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 2
+#define GEMM_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -151,6 +151,29 @@ GEMM_API int gemm_naive_f32(int M, int N, int K, float alpha, float beta,
                    const float *A, const float *B, float *C, void *stream);
 GEMM_API int gemm_naive_bf16(int M, int N, int K, float alpha, float beta,
                     const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/*
+ * Sum of a float32 vector, the memory-bound case study of page "Memory
+ * hierarchy and cost table", section 4.7 (summing 100 million floats):
+ *
+ *     *out = x[0] + x[1] + ... + x[n-1]
+ *
+ * x and out are device pointers (x: n floats, 4-byte aligned, read-only;
+ * out: one float, written), owned by the caller.  Sums are fp32 in a fixed
+ * order, so repeated calls give identical bits; no element passes through
+ * more than n / 2^21 + 32 fp32 additions (reduce_sum_f32; ceil(log2 n) for
+ * the naive form), which bounds the rounding error by that many units of
+ * 2^-24 times sum |x|.  n == 0 writes 0.  Asynchronous like the GEMMs; negative n, a NULL out, a NULL x
+ * with n > 0 or a misaligned x return GEMM_ERR_INVALID_ARG and launch
+ * nothing.  Uses the stream's workspace (as the GEMMs' split-K does).
+ * reduce_sum_f32 is the optimised form (16-byte loads, one workgroup per
+ * contiguous chunk); reduce_sum_f32_naive is the page's first version (one
+ * element per thread, a shared-memory tree per 256 elements) with the
+ * global atomic replaced by further tree passes; it can sum up to 2^31
+ * elements.
+ */
+GEMM_API int reduce_sum_f32(const float *x, int64_t n, float *out, void *stream);
+GEMM_API int reduce_sum_f32_naive(const float *x, int64_t n, float *out, void *stream);
 
 /* Static English text for a gemm_status value (never NULL). */
 GEMM_API const char *gemm_status_string(int status);

@@ -57,6 +57,10 @@ def library():
             fn = getattr(lib, name)
             fn.argtypes = [i, i, i, f, f, vp, vp, vp, vp, i, vp]
             fn.restype = ctypes.c_int
+        for name in ("reduce_sum_f32", "reduce_sum_f32_naive"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, ctypes.c_int64, vp, vp]
+            fn.restype = ctypes.c_int
         lib.gemm_status_string.argtypes = [ctypes.c_int]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_last_kernel.argtypes = []
@@ -171,6 +175,27 @@ def gemm_naive_f32(A, B, C, alpha=1.0, beta=0.0, stream=None):
 def gemm_naive_bf16(A, B, C, alpha=1.0, beta=0.0, stream=None):
     import torch
     return _call("gemm_naive_bf16", A, B, C, alpha, beta, stream, torch.bfloat16)
+
+
+def reduce_sum_f32(x, out, stream=None, naive=False):
+    """out[0] = sum of the float32 vector x (both on the GPU; out holds one
+    float32).  ``naive`` runs the one-element-per-thread first version."""
+    import torch
+    for name, t in (("x", x), ("out", out)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+            raise TypeError("%s must be a float32 tensor" % name)
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if out.numel() < 1 or x.device != out.device:
+        raise ValueError("out must hold one float on x's device")
+    lib = library()
+    fn = lib.reduce_sum_f32_naive if naive else lib.reduce_sum_f32
+    with torch.cuda.device(x.device):
+        status = fn(ctypes.c_void_p(x.data_ptr()), x.numel(), ctypes.c_void_p(out.data_ptr()),
+                    _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
+    return out
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):

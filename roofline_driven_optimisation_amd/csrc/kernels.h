@@ -120,6 +120,20 @@ hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
                                   float *partials, int *counters, int counter_ints,
                                   char *xcd_base, int xcd_group, const Epi &epi,
                                   hipStream_t stream);
+// Sum of a float32 vector (4-byte aligned, any length) into *out, on the
+// device.  blocks <= kReduceMaxBlocks workgroups each stream a contiguous
+// chunk; with blocks > 1 they reduce through `partials` (blocks floats) and
+// `counter` (one int, zero on entry and left zero), both uncached memory.
+constexpr int kReduceMaxBlocks = 2048;
+long long reduce_blocks(long long n, int num_cus);
+hipError_t launch_reduce_sum(const float *x, long long n, float *out, float *partials,
+                             int *counter, int blocks, hipStream_t stream);
+// The ladder's first rung: one element per thread, an LDS tree per 256,
+// relaunched on its partials (two halves of `scratch`, ping-pong) until one
+// value is left.  Needs 2 * ceil(n / 256) scratch floats when n > 256.
+hipError_t launch_reduce_sum_tree(const float *x, long long n, float *out, float *scratch,
+                                  long long scratch_floats, hipStream_t stream);
+
 // Runs a probe grid on `stream`, waits for it, and sets *ok when every
 // workgroups whose ids are equal modulo kXcdCount ran on one XCD and the
 // kXcdCount residues on different XCDs (which XCD takes workgroup 0 varies

@@ -147,3 +147,15 @@ def gemm_roofline(M: int, N: int, K: int, dtype: str, beta_nonzero: bool,
     else:
         bound = "mfma" if dtype == "bf16" else "fp32"
     return Roofline(flops, nbytes, ai, peak, MI355X_PEAK_HBM, bound, att)
+
+
+def sum_roofline(n: int) -> Roofline:
+    """Roofline position of summing n float32 values (page "Memory hierarchy
+    and cost table", section 4.7): n - 1 additions (counted as n) against 4n
+    bytes read and one float written, AI 1/4, far left of every ridge, so
+    HBM-bound.  The fp32 VALU peak is the compute roof."""
+    flops = max(n, 1)
+    nbytes = 4 * n + 4
+    ai = flops / nbytes
+    return Roofline(flops, nbytes, ai, MI355X_PEAK_FP32, MI355X_PEAK_HBM, "hbm",
+                    attainable(MI355X_PEAK_FP32, MI355X_PEAK_HBM, ai))
