@@ -171,6 +171,31 @@ class Oracle:
             return self.epilogue(out, den, bias, act, cols=cols)
         return out, den
 
+    def gemm_batched(self, A, B, C=None, alpha=1.0, beta=0.0, bf16=False, trans_b=False):
+        """Strided batched GEMM, item by item: A (batch, M, K), B (batch, K, N)
+        or, with ``trans_b``, (batch, N, K) holding each item's B transposed;
+        C (batch, M, N) or None.  Returns (C_ref, den) of shape (batch, M, N).
+        This is the attention use of the GEMM: S = Q K^T and O = P V (page
+        "From model computation to GPU execution", section 1.2), one GEMM per
+        head (page "Naive GEMM and Roofline analysis", section 10.1), with K
+        stored token-major (Seq_k x d), i.e. as B transposed.  One plain GEMM
+        per item."""
+        A = np.asarray(A)
+        B = np.asarray(B)
+        if A.ndim != 3 or B.ndim != 3 or A.shape[0] != B.shape[0]:
+            raise ValueError("A and B must be (batch, rows, cols) with one batch size")
+        outs, dens = [], []
+        for b in range(A.shape[0]):
+            Bb = np.ascontiguousarray(B[b].T) if trans_b else B[b]
+            Cb = None if C is None else C[b]
+            r, d = self.gemm(A[b], Bb, Cb, alpha, beta, bf16)
+            outs.append(r)
+            dens.append(d)
+        M, N = A.shape[1], (B.shape[1] if trans_b else B.shape[2])
+        if not outs:
+            return np.zeros((0, M, N)), np.zeros((0, M, N))
+        return np.stack(outs), np.stack(dens)
+
     def sum_f32(self, x):
         """fp64 sum of a float32 vector and its sum of magnitudes (the
         reduction case study of page "Memory hierarchy and cost table",
@@ -213,6 +238,10 @@ def epilogue(z, den, bias=None, act=0, cols=None):
 
 def sum_f32(x):
     return default().sum_f32(x)
+
+
+def gemm_batched(A, B, C=None, alpha=1.0, beta=0.0, bf16=False, trans_b=False):
+    return default().gemm_batched(A, B, C, alpha, beta, bf16, trans_b)
 
 
 def num_threads() -> int:

@@ -295,13 +295,30 @@ def pin_sum_precision(o):
     assert abs(a - math.fsum(np.abs(x.astype(np.float64)))) <= 1e-12 * a
 
 
+def pin_batched(o):
+    """Strided batched form: a stored transpose with trans_b equals the plain
+    product (the indexing of B^T), every item equals its own single GEMM
+    on hand values, and items do not mix."""
+    A = np.stack([_mat([[1, 2], [3, 4]]), _mat([[0, 1], [1, 0]])])
+    B = np.stack([_mat([[5, 6, 7], [8, 9, 10]]), _mat([[1, 2, 3], [4, 5, 6]])])
+    got, _ = o.gemm_batched(A, B)
+    assert np.array_equal(got[0], [[21, 24, 27], [47, 54, 61]])
+    assert np.array_equal(got[1], [[4, 5, 6], [1, 2, 3]])  # a row swap
+    Bt = np.ascontiguousarray(np.transpose(B, (0, 2, 1)))
+    got_t, _ = o.gemm_batched(A, Bt, trans_b=True)
+    assert np.array_equal(got_t, got)
+    C = np.stack([_mat([[1, 1, 1], [1, 1, 1]]), _mat([[2, 0, 2], [0, 2, 0]])])
+    got_c, _ = o.gemm_batched(A, Bt, C, alpha=2.0, beta=0.5, trans_b=True)
+    assert np.array_equal(got_c, 2.0 * got + 0.5 * C.astype(np.float64))
+
+
 ALL_PINS = [
     pin_hand_signs, pin_rectangular_hand, pin_identity_zero_permutation, pin_all_ones,
     pin_alpha_beta_linearity, pin_transpose_identity, pin_brute_force_integers,
     pin_random_floats_vs_numpy, pin_bf16_widening, pin_beta_zero_reads_no_c, pin_k_zero,
     pin_entries_match_full, pin_entries_hand, pin_den_bounds_result,
     pin_epilogue_closed_forms, pin_epilogue_bias_columns, pin_epilogue_gemm, pin_epilogue_slope,
-    pin_sum_closed_forms, pin_sum_precision,
+    pin_sum_closed_forms, pin_sum_precision, pin_batched,
 ]
 
 
