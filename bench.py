@@ -47,7 +47,8 @@ HEADLINE = "bf16_4096"
 SECONDARY = ["f32_4096", "f32_4092", "prefill_qkv", "prefill_o", "prefill_gate_up",
              "prefill_down", "decode_up_m1", "decode_up_m8", "decode_up_m16",
              "decode_down_m1", "decode_down_m8", "decode_down_m16", "decode_lm_head",
-             "prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu", "sum_1e8"]
+             "prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu", "sum_1e8",
+             "attn_qk", "attn_pv"]
 # "<workload>+bias_<act>": the workload through the fused Linear-layer
 # epilogue, C = act(A*B + bias) with a normal(0, 0.5) bias over the columns
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
@@ -161,8 +162,53 @@ class PreparedSum:
         return binding.last_kernel()
 
 
+# attention GEMMs of one layer: 32 heads, 2048 tokens, head dimension 128
+ATTENTION = {"attn_qk": (32, 2048, 2048, 128, True), "attn_pv": (32, 2048, 128, 2048, False)}
+
+
+class PreparedBatched:
+    """Strided batched bf16 GEMM: S = Q K^T (K stored token-major, so B is
+    transposed) or O = P V, per head; Q, K, V ~ normal(0, 1) and P ~
+    uniform[0, 1/64] rounded to bf16 (seed 0), rotated across copies."""
+
+    def __init__(self, name: str, seed: int = 0):
+        import torch
+        from roofline_driven_optimisation_amd.inputs import f32_to_bf16_bits
+        self.name = name
+        self.batch, self.M, self.N, self.K, self.trans_b = ATTENTION[name]
+        rng = np.random.default_rng(seed)
+        b, M, N, K = self.batch, self.M, self.N, self.K
+        if self.trans_b:
+            a = rng.standard_normal((b, M, K)).astype(np.float32)
+            bb = rng.standard_normal((b, N, K)).astype(np.float32)
+        else:
+            a = rng.uniform(0.0, 1.0 / 64, (b, M, K)).astype(np.float32)
+            bb = rng.standard_normal((b, K, N)).astype(np.float32)
+        A = torch.from_numpy(f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+        B = torch.from_numpy(f32_to_bf16_bits(bb).view(np.int16)).view(torch.bfloat16).cuda()
+        C = torch.zeros(b, M, N, dtype=torch.float32, device="cuda")
+        per_set = 2 * (A.numel() + B.numel()) + 4 * C.numel()
+        self.sets = max(1, -(-ROTATE_BYTES // per_set))
+        self.bufs = [(A, B, C)] + [(A.clone(), B.clone(), C.clone()) for _ in range(self.sets - 1)]
+        self.rf = rl.batched_gemm_roofline(b, M, N, K, "bf16")
+
+    def launch(self, i: int, naive: bool = False):
+        from roofline_driven_optimisation_amd import binding
+        A, B, C = self.bufs[i % self.sets]
+        binding.gemm_bf16_batched(A, B, C, 1.0, 0.0, trans_b=self.trans_b)
+
+    def kernel_name(self) -> str:
+        from roofline_driven_optimisation_amd import binding
+        self.launch(0)
+        return binding.last_kernel()
+
+
 def prepare(name: str):
-    return PreparedSum(name) if name.startswith("sum_") else Prepared(name)
+    if name.startswith("sum_"):
+        return PreparedSum(name)
+    if name in ATTENTION:
+        return PreparedBatched(name)
+    return Prepared(name)
 
 
 SETTLE_S = 0.1  # minimum untimed warm-up, seconds
@@ -204,6 +250,12 @@ def summary(p, sec: float, kname: str) -> dict:
     if isinstance(p, PreparedSum):
         return {"workload": p.name, "n": p.n, "dtype": "f32", "kernel": kname,
                 "us": round(sec * 1e6, 2), "gbs": round(gbs, 1), "bound": p.rf.bound,
+                "frac": round(p.rf.fraction(sec), 4)}
+    if isinstance(p, PreparedBatched):
+        return {"workload": p.name, "batch": p.batch, "M": p.M, "N": p.N, "K": p.K,
+                "trans_b": p.trans_b, "dtype": "bf16", "kernel": kname,
+                "us": round(sec * 1e6, 2), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+                "bound": p.rf.bound, "roofline_tflops": round(p.rf.attainable / 1e12, 1),
                 "frac": round(p.rf.fraction(sec), 4)}
     return {
         "workload": p.name, "M": p.w.M, "N": p.w.N, "K": p.w.K, "dtype": p.w.dtype,

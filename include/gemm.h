@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 3
+#define GEMM_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -151,6 +151,33 @@ GEMM_API int gemm_naive_f32(int M, int N, int K, float alpha, float beta,
                    const float *A, const float *B, float *C, void *stream);
 GEMM_API int gemm_naive_bf16(int M, int N, int K, float alpha, float beta,
                     const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/*
+ * Strided batched bf16 GEMM, the shape attention gives the GEMM: S = Q K^T
+ * and O = P V (page "From model computation to GPU execution", section
+ * 1.2), one product per head (page "Naive GEMM and Roofline analysis",
+ * section 10.1).  For b = 0 .. batch-1:
+ *
+ *     C_b = alpha * A_b * op(B_b) + beta * C_b
+ *
+ * A_b = A + b * stride_a is M x K row-major; B_b = B + b * stride_b is
+ * K x N row-major (trans_b == 0, op = identity) or N x K row-major
+ * (trans_b == 1, op = transpose: a key matrix stored token by token);
+ * C_b = C + b * stride_c is M x N float32.  Strides count elements; A and B
+ * strides may be 0 (one operand shared by every item), stride_c must be at
+ * least M * N when batch > 1.  Device pointers, caller-owned, asynchronous.
+ * Items run in one launch of the four-wave 256 x 256 kernel (or the
+ * 128 x 128 one when N <= 128 and B is not transposed) when K % 8 == 0,
+ * N % 8 == 0 (B not transposed), A and B are 16-byte aligned with strides
+ * that are multiples of 8; otherwise a one-thread-per-output kernel.  No
+ * split-K and no fused epilogue here.  batch < 0, batch > 65535, trans_b
+ * not 0 or 1, negative strides, overlapping C items and the gemm_bf16
+ * argument errors return GEMM_ERR_INVALID_ARG.
+ */
+GEMM_API int gemm_bf16_strided_batched(int batch, int M, int N, int K, float alpha, float beta,
+                                       const uint16_t *A, int64_t stride_a,
+                                       const uint16_t *B, int64_t stride_b, int trans_b,
+                                       float *C, int64_t stride_c, void *stream);
 
 /*
  * Sum of a float32 vector, the memory-bound case study of page "Memory

@@ -57,6 +57,9 @@ def library():
             fn = getattr(lib, name)
             fn.argtypes = [i, i, i, f, f, vp, vp, vp, vp, i, vp]
             fn.restype = ctypes.c_int
+        lib.gemm_bf16_strided_batched.argtypes = [i, i, i, i, f, f, vp, ctypes.c_int64, vp,
+                                                  ctypes.c_int64, i, vp, ctypes.c_int64, vp]
+        lib.gemm_bf16_strided_batched.restype = ctypes.c_int
         for name in ("reduce_sum_f32", "reduce_sum_f32_naive"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, ctypes.c_int64, vp, vp]
@@ -175,6 +178,35 @@ def gemm_naive_f32(A, B, C, alpha=1.0, beta=0.0, stream=None):
 def gemm_naive_bf16(A, B, C, alpha=1.0, beta=0.0, stream=None):
     import torch
     return _call("gemm_naive_bf16", A, B, C, alpha, beta, stream, torch.bfloat16)
+
+
+def gemm_bf16_batched(A, B, C, alpha=1.0, beta=0.0, trans_b=False, stream=None):
+    """C[b] = alpha*A[b]@op(B[b]) + beta*C[b] for 3-D contiguous tensors:
+    A (batch, M, K) bfloat16, B (batch, K, N) or with trans_b (batch, N, K)
+    bfloat16, C (batch, M, N) float32."""
+    import torch
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 3-D tensor" % name)
+        if t.device.type != "cuda" or t.device != C.device:
+            raise ValueError("%s must be on C's GPU" % name)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16 or C.dtype != torch.float32:
+        raise TypeError("A and B must be bfloat16 and C float32")
+    batch, M, K = A.shape
+    N = B.shape[1] if trans_b else B.shape[2]
+    Kb = B.shape[2] if trans_b else B.shape[1]
+    if B.shape[0] != batch or Kb != K or tuple(C.shape) != (batch, M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    lib = library()
+    with torch.cuda.device(C.device):
+        status = lib.gemm_bf16_strided_batched(
+            int(batch), int(M), int(N), int(K), float(alpha), float(beta),
+            ctypes.c_void_p(A.data_ptr()), M * K, ctypes.c_void_p(B.data_ptr()), K * N,
+            1 if trans_b else 0, ctypes.c_void_p(C.data_ptr()), M * N, _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
+    return C
 
 
 def reduce_sum_f32(x, out, stream=None, naive=False):

@@ -401,13 +401,21 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
                                                                 const uint16_t *__restrict__ A,
                                                                 const uint16_t *__restrict__ B,
                                                                 float *C, int tiles_m,
-                                                                int tiles_n, Epi epi) {
+                                                                int tiles_n, Epi epi,
+                                                                Batch batch) {
     using T = Tile<BM, BN>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][T::A_STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][T::B_STAGE];
 
+    // XCD-aware order over the tiles of all items (one item: the plain GEMM)
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
+    const int v = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_item = tiles_m * tiles_n;
+    const int item = v / per_item;
+    A += item * batch.stride_a;
+    B += item * batch.stride_b;
+    C += item * batch.stride_c;
+    grouped_tile(v - item * per_item, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x;
@@ -949,13 +957,14 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
 // (a K tail) are skipped per step.  The epilogue stages each wave's tile
 // through LDS (store_c_tile_lds128), about 1 % faster than direct 16-byte
 // stores.
-template <bool KTAIL, bool EPI>
+template <bool KTAIL, bool EPI, bool TRANSB>
 __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, float alpha,
                                                          float beta,
                                                          const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B, float *C,
                                                          int tiles_m, int tiles_n,
-                                                         PPSplit split_plan, Epi epi) {
+                                                         PPSplit split_plan, Epi epi,
+                                                         Batch batch) {
     constexpr int BM = 256, BN = 256, S = 4, BK = kPPBK;
     constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
@@ -984,8 +993,15 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
         v = split_plan.split_from + (q >> 1);
         split = q & 1;
     }
+    // A batched launch (never split) numbers the tiles of all items in
+    // turn: the XCD-aware order keeps one item's tiles on one XCD.
+    const int per_item = tiles_m * tiles_n;
+    const int item = v / per_item;
+    A += item * batch.stride_a;
+    B += item * batch.stride_b;
+    C += item * batch.stride_c;
     int tm, tn;
-    grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
+    grouped_tile(v - item * per_item, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int total_steps = (K + BK - 1) / BK;
     const int t_begin = split == 1 ? split_plan.split_step : 0;
@@ -1010,13 +1026,20 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
         uint32_t la, lb;
         bool a_ok;
     };
+    // TRANSB: B is stored N x K (row n holds B[.][n] along k), so its tile
+    // (256 rows n, 32 k) is copied and laid out exactly like A's tile.
+    static_assert(!TRANSB || B_LOADS == A_LOADS, "a transposed B tile copies like A's");
     auto step_copy = [&](int t) {  // t counts this workgroup's steps
         const int k0 = (t_begin + t) * BK, stage = t % S;
         StepCopy c;
         c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
                          (static_cast<long long>(M - m0) * K - k0) * 2);
-        c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
-                         (static_cast<long long>(K - k0) * N - n0) * 2);
+        if constexpr (TRANSB)
+            c.rb = make_desc(B + static_cast<size_t>(n0) * K + k0,
+                             (static_cast<long long>(N - n0) * K - k0) * 2);
+        else
+            c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                             (static_cast<long long>(K - k0) * N - n0) * 2);
         c.a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
         c.la = lds_address(&lds_a[stage][wave * 512]);
         c.lb = lds_address(&lds_b[stage][wave * 512]);
@@ -1025,6 +1048,9 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     auto issue_copy = [&](const StepCopy &c, int q) {
         if (q < A_LOADS)
             lds_dma16(c.ra, c.la + q * 4 * 1024, c.a_ok ? a_off + q * a_step : kOOB);
+        else if constexpr (TRANSB)
+            lds_dma16(c.rb, c.lb + (q - A_LOADS) * 4 * 1024,
+                      c.a_ok ? a_off + (q - A_LOADS) * a_step : kOOB);
         else
             lds_dma16(c.rb, c.lb + (q - A_LOADS) * 4 * 1024,
                       b_ok ? b_off + (q - A_LOADS) * b_step : kOOB);
@@ -1035,13 +1061,23 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     const int b_col_lane = wn * WN + 16 * (g & 1) + 4 * (j16 & 3);
     const int b_row_lane = 8 * (g >> 1) + (j16 >> 2);
     typedef short s16x8 __attribute__((ext_vector_type(8)));
-    constexpr int kReads = MI + 2 * NI;
+    // fragment reads per sub-step: one per A block, and per B block two
+    // transposing reads (B as K x N) or one plain read (TRANSB)
+    constexpr int kBReads = TRANSB ? 1 : 2;
+    constexpr int kReads = MI + kBReads * NI;
+    const int b_lane_base = (wn * WN + l32) * BK;  // TRANSB: row n of the B tile
     auto read_one = [&](int stage, int s, int q, bf16x8 (&a)[MI], s16x8 (&b)[NI]) {
         if (q < MI) {
             const int pos = ((2 * s + h) ^ swz_a32(l32)) * 8;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(
                 &lds_a[stage][a_lane_base + 32 * q * BK + pos]);
             a[q] = __builtin_bit_cast(bf16x8, v);
+        } else if constexpr (TRANSB) {
+            const int jj = q - MI;
+            const int pos = ((2 * s + h) ^ swz_a32(l32)) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                &lds_b[stage][b_lane_base + 32 * jj * BK + pos]);
+            b[jj] = __builtin_bit_cast(s16x8, v);
         } else {
             const int jj = (q - MI) >> 1, r = (q - MI) & 1;
             const int row = 16 * s + 4 * r + b_row_lane;
@@ -1054,10 +1090,10 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
             for (int e = 0; e < 4; ++e) b[jj][4 * r + e] = part[e];
         }
     };
-    // reads in consumption order: B block 0 (two halves), every A block,
-    // then the other B blocks
+    // reads in consumption order: B block 0, every A block, then the other
+    // B blocks
     auto read_in_order = [&](int stage, int s, int r, bf16x8 (&a)[MI], s16x8 (&b)[NI]) {
-        const int q = r < 2 ? MI + r : (r < 2 + MI ? r - 2 : r);
+        const int q = r < kBReads ? MI + r : (r < kBReads + MI ? r - kBReads : r);
         read_one(stage, s, q, a, b);
     };
 
@@ -1261,33 +1297,44 @@ bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan) {
 
 hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                      const uint16_t *B, float *C, const PPSplit *split, const Epi &epi,
-                     hipStream_t stream) {
+                     hipStream_t stream, const Batch &batch = kOneItem, bool trans_b = false) {
     const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const long long tiles = tiles_m * tiles_n;
-    if (tiles > 0x3fffffffLL) return hipErrorInvalidValue;
+    const long long total = tiles * batch.items;
+    if (total > 0x3fffffffLL || batch.items < 1 || (batch.items > 1 && split != nullptr))
+        return hipErrorInvalidValue;
     PPSplit plan;
-    if (!make_plan(split, tiles, K, plan)) return hipErrorInvalidValue;
-    const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
-    with_flags(K % kPPBK != 0, epi_on(epi), [&](auto ktail, auto e) {
-        bf16_q4_kernel<decltype(ktail)::value, decltype(e)::value>
+    if (!make_plan(split, total, K, plan)) return hipErrorInvalidValue;
+    const long long grid = plan.split_from + 2 * (total - plan.split_from);
+    auto go = [&](auto ktail, auto e, auto tb) {
+        bf16_q4_kernel<decltype(ktail)::value, decltype(e)::value, decltype(tb)::value>
             <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
                 M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
-                static_cast<int>(tiles_n), plan, epi);
-    });
+                static_cast<int>(tiles_n), plan, epi, batch);
+    };
+    if (trans_b) {
+        if (epi_on(epi)) return hipErrorInvalidValue;  // no fused epilogue in batched calls
+        if (K % kPPBK != 0) go(std::true_type(), std::false_type(), std::true_type());
+        else go(std::false_type(), std::false_type(), std::true_type());
+    } else {
+        with_flags(K % kPPBK != 0, epi_on(epi),
+                   [&](auto ktail, auto e) { go(ktail, e, std::false_type()); });
+    }
     return hipGetLastError();
 }
 
 template <int BM, int BN>
 hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16_t *A,
-                      const uint16_t *B, float *C, const Epi &epi, hipStream_t stream) {
+                      const uint16_t *B, float *C, const Epi &epi, hipStream_t stream,
+                      const Batch &batch = kOneItem) {
     const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const long long tiles = tiles_m * tiles_n;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long tiles = tiles_m * tiles_n * batch.items;
+    if (tiles > 0x7fffffffLL || batch.items < 1) return hipErrorInvalidValue;
     with_flags(K % kBK != 0, epi_on(epi), [&](auto ktail, auto e) {
         bf16_mfma_kernel<BM, BN, decltype(ktail)::value, decltype(e)::value>
             <<<dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream>>>(
                 M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
-                static_cast<int>(tiles_n), epi);
+                static_cast<int>(tiles_n), epi, batch);
     });
     return hipGetLastError();
 }
@@ -1358,6 +1405,20 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
         }
     }
     return best;
+}
+
+hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
+                               const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
+                               bool trans_b, hipStream_t stream) {
+    switch (cfg) {
+        case 0:
+            return launch_q4(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
+                             trans_b);
+        case 3:
+            if (trans_b) return hipErrorInvalidValue;
+            return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, kNoEpi, stream, batch);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,

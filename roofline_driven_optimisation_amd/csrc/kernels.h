@@ -20,6 +20,14 @@ struct Epi {
 inline bool epi_on(const Epi &e) { return e.bias != nullptr || e.act != kActNone; }
 constexpr Epi kNoEpi = {nullptr, kActNone};
 
+// Strided batch of independent GEMMs: item b uses A + b stride_a, B + b
+// stride_b and C + b stride_c (elements).  {1, 0, 0, 0} is a single GEMM.
+struct Batch {
+    int items;
+    long long stride_a, stride_b, stride_c;
+};
+constexpr Batch kOneItem = {1, 0, 0, 0};
+
 // One thread per output element (the unoptimised starting point).
 hipError_t launch_naive_f32(int M, int N, int K, float alpha, float beta, const float *A,
                             const float *B, float *C, const Epi &epi, hipStream_t stream);
@@ -80,6 +88,18 @@ int bf16_pp_split_tiles(int M, int N, int K, int num_cus);    // 0: no split
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
                             const Epi &epi, hipStream_t stream);
+// Strided batched bf16 GEMM on the tiled kernels, no split and no fused
+// epilogue: `cfg` 0 (the four-wave 256 x 256 kernel, which also takes a B
+// stored transposed, N x K, when trans_b) or 3 (128 x 128, B as K x N).  The
+// same shape requirements as launch_bf16_mfma, for every item (strides keep
+// each item 16-byte aligned).
+hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
+                               const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
+                               bool trans_b, hipStream_t stream);
+// One thread per output element, any layout: the batched fallback.
+hipError_t launch_naive_bf16_batched(int M, int N, int K, float alpha, float beta,
+                                     const uint16_t *A, const uint16_t *B, float *C,
+                                     const Batch &batch, bool trans_b, hipStream_t stream);
 
 // Skinny-M (M <= 16) bf16 kernel that streams B once from HBM.  Needs
 // K % 8 == 0, N % 8 == 0 and 16-byte aligned A, B and C.  With splits > 1 the

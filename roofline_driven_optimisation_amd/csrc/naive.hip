@@ -40,6 +40,32 @@ __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float a
     C[idx] = epi_apply<EPI>(out, EPI && epi.bias ? epi.bias[col] : 0.0f, epi.act);
 }
 
+// The batched fallback: item blockIdx.y, B stored K x N, or N x K with TRANSB.
+template <bool TRANSB>
+__global__ __launch_bounds__(256) void naive_batched_kernel(int M, int N, int K, float alpha,
+                                                            float beta, const uint16_t *A,
+                                                            const uint16_t *B, float *C,
+                                                            int tiles_n, Batch batch) {
+    const long long item = blockIdx.y;
+    A += item * batch.stride_a;
+    B += item * batch.stride_b;
+    C += item * batch.stride_c;
+    const int tile = blockIdx.x;
+    const int row = (tile / tiles_n) * 16 + threadIdx.y;
+    const int col = (tile % tiles_n) * 16 + threadIdx.x;
+    if (row >= M || col >= N) return;
+    const uint16_t *a = A + static_cast<size_t>(row) * K;
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const size_t bi = TRANSB ? static_cast<size_t>(col) * K + k : static_cast<size_t>(k) * N + col;
+        sum = fmaf(bf16_bits_to_float(a[k]), bf16_bits_to_float(B[bi]), sum);
+    }
+    const size_t idx = static_cast<size_t>(row) * N + col;
+    float out = alpha * sum;
+    if (beta != 0.0f) out = fmaf(beta, C[idx], out);
+    C[idx] = out;
+}
+
 template <bool EPI>
 __global__ __launch_bounds__(256) void scale_kernel(size_t count, int N, float beta, float *C,
                                                     Epi epi) {
@@ -81,6 +107,24 @@ hipError_t launch_naive_f32(int M, int N, int K, float alpha, float beta, const 
 hipError_t launch_naive_bf16(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                              const uint16_t *B, float *C, const Epi &epi, hipStream_t stream) {
     return launch_naive<uint16_t>(M, N, K, alpha, beta, A, B, C, epi, stream);
+}
+
+hipError_t launch_naive_bf16_batched(int M, int N, int K, float alpha, float beta,
+                                     const uint16_t *A, const uint16_t *B, float *C,
+                                     const Batch &batch, bool trans_b, hipStream_t stream) {
+    const long long tiles_m = (M + 15) / 16, tiles_n = (N + 15) / 16;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL || batch.items < 1 || batch.items > 65535)
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(batch.items)),
+        block(16, 16);
+    if (trans_b)
+        naive_batched_kernel<true><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                               static_cast<int>(tiles_n), batch);
+    else
+        naive_batched_kernel<false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                                static_cast<int>(tiles_n), batch);
+    return hipGetLastError();
 }
 
 hipError_t launch_scale_c(int M, int N, float beta, float *C, const Epi &epi,

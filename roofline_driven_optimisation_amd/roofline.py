@@ -159,3 +159,17 @@ def sum_roofline(n: int) -> Roofline:
     ai = flops / nbytes
     return Roofline(flops, nbytes, ai, MI355X_PEAK_FP32, MI355X_PEAK_HBM, "hbm",
                     attainable(MI355X_PEAK_FP32, MI355X_PEAK_HBM, ai))
+
+
+def batched_gemm_roofline(batch: int, M: int, N: int, K: int, dtype: str) -> Roofline:
+    """A batch of independent GEMMs (beta = 0, fp32 C): batch times the
+    FLOPs and compulsory bytes of one.  Attention's S = Q K^T with d = 128
+    lands left of the ridge: writing the fp32 scores outweighs the MFMA work."""
+    one = gemm_roofline(M, N, K, dtype, False)
+    flops = batch * one.flops
+    nbytes = batch * one.nbytes
+    ai = flops / nbytes
+    peak = one.peak_compute
+    att = attainable(peak, MI355X_PEAK_HBM, ai)
+    bound = "hbm" if MI355X_PEAK_HBM * ai < peak else one.bound
+    return Roofline(flops, nbytes, ai, peak, MI355X_PEAK_HBM, bound, att)
