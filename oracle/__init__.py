@@ -63,6 +63,11 @@ class Oracle:
             fn.restype = ctypes.c_int
         lib.oracle_epilogue.argtypes = [i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp]
         lib.oracle_epilogue.restype = ctypes.c_int
+        lib.oracle_fp8_decode.argtypes = [i64, vp, ctypes.c_int, vp]
+        lib.oracle_fp8_decode.restype = ctypes.c_int
+        lib.oracle_gemm_fp8.argtypes = [i64, i64, i64, f64, f64, f64, f64, ctypes.c_int,
+                                        vp, vp, vp, vp, vp]
+        lib.oracle_gemm_fp8.restype = ctypes.c_int
         lib.oracle_sum_f32.argtypes = [i64, vp, vp, vp]
         lib.oracle_sum_f32.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
@@ -196,6 +201,39 @@ class Oracle:
             return np.zeros((0, M, N)), np.zeros((0, M, N))
         return np.stack(outs), np.stack(dens)
 
+    def fp8_decode(self, b, fmt=0):
+        """Exact values (float64) of 8-bit float bytes: fmt 0 E4M3, 1 E5M2."""
+        b = np.ascontiguousarray(b, dtype=np.uint8)
+        out = np.empty(b.shape, dtype=np.float64)
+        rc = self.lib.oracle_fp8_decode(b.size, _ptr(b), int(fmt), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle rejected the decode arguments (code %d)" % rc)
+        return out
+
+    def gemm_fp8(self, A, B, C=None, alpha=1.0, beta=0.0, sa=1.0, sb=1.0, fmt=0):
+        """fp64 reference of the 8-bit float GEMM: A (M x K) and B stored
+        N x K as uint8 bytes, C fp32 (read when beta != 0):
+        alpha sa sb A B^T + beta C.  Returns (C_ref, den)."""
+        A = np.ascontiguousarray(A, dtype=np.uint8)
+        B = np.ascontiguousarray(B, dtype=np.uint8)
+        if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[1]:
+            raise ValueError("A is M x K and B is N x K")
+        M, K = A.shape
+        N = B.shape[0]
+        if beta != 0.0:
+            C = np.ascontiguousarray(C, dtype=np.float32)
+            if C.shape != (M, N):
+                raise ValueError("C_in must be %dx%d" % (M, N))
+        else:
+            C = None
+        Cref = np.empty((M, N), dtype=np.float64)
+        den = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_gemm_fp8(M, N, K, float(alpha), float(beta), float(sa), float(sb),
+                                      int(fmt), _ptr(A), _ptr(B), _ptr(C), _ptr(Cref), _ptr(den))
+        if rc != 0:
+            raise ValueError("oracle rejected the fp8 arguments (code %d)" % rc)
+        return Cref, den
+
     def sum_f32(self, x):
         """fp64 sum of a float32 vector and its sum of magnitudes (the
         reduction case study of page "Memory hierarchy and cost table",
@@ -238,6 +276,14 @@ def epilogue(z, den, bias=None, act=0, cols=None):
 
 def sum_f32(x):
     return default().sum_f32(x)
+
+
+def fp8_decode(b, fmt=0):
+    return default().fp8_decode(b, fmt)
+
+
+def gemm_fp8(A, B, C=None, alpha=1.0, beta=0.0, sa=1.0, sb=1.0, fmt=0):
+    return default().gemm_fp8(A, B, C, alpha, beta, sa, sb, fmt)
 
 
 def gemm_batched(A, B, C=None, alpha=1.0, beta=0.0, bf16=False, trans_b=False):

@@ -182,6 +182,76 @@ int oracle_gemm_bf16_entries(int64_t M, int64_t N, int64_t K, double alpha, doub
 }
 
 /*
+ * 8-bit floating-point inputs (the "smaller dtype raises the arithmetic
+ * intensity" step of page "Where kernel performance comes from", section on
+ * GEMM: 1-byte operands halve the bytes per multiply-add of bf16).  Two
+ * formats, decoded exactly to double from their definitions:
+ *   fmt 0, E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ *          0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinity;
+ *   fmt 1, E5M2: sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent
+ *          0 is subnormal (m/4 * 2^-14); exponent 31 is infinity (m = 0) or
+ *          NaN.
+ * The GEMM takes B stored N x K (row n holds column n of the product's
+ * right operand, K contiguous) and per-tensor scales:
+ *   C_ref[m][n] = alpha * sa * sb * sum_k A[m][k] * B[n][k] + beta * C_in[m][n]
+ * with den = |alpha sa sb| * sum_k |A[m][k] B[n][k]| + |beta C_in| + 1e-30.
+ */
+static double fp8_value(uint8_t b, int fmt)
+{
+    const int s = b >> 7;
+    double v;
+    if (fmt == 0) {
+        const int e = (b >> 3) & 15, m = b & 7;
+        if (e == 15 && m == 7)
+            return NAN;
+        v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    } else {
+        const int e = (b >> 2) & 31, m = b & 3;
+        if (e == 31)
+            return m == 0 ? (s ? -INFINITY : INFINITY) : NAN;
+        v = e == 0 ? ldexp(m / 4.0, -14) : ldexp(1.0 + m / 4.0, e - 15);
+    }
+    return s ? -v : v;
+}
+
+int oracle_fp8_decode(int64_t n, const uint8_t *bytes, int fmt, double *out)
+{
+    if (n < 0 || (fmt != 0 && fmt != 1) || (n > 0 && (bytes == NULL || out == NULL)))
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = fp8_value(bytes[i], fmt);
+    return ORACLE_OK;
+}
+
+int oracle_gemm_fp8(int64_t M, int64_t N, int64_t K, double alpha, double beta, double sa,
+                    double sb, int fmt, const uint8_t *A, const uint8_t *B, const float *Cin,
+                    double *Cref, double *den)
+{
+    if (fmt != 0 && fmt != 1)
+        return ORACLE_EINVAL;
+    int rc = check_args(M, N, K, beta, A, B, Cin, Cref, den);
+    if (rc != ORACLE_OK || M == 0 || N == 0)
+        return rc;
+    const double scale = alpha * sa * sb;
+    int64_t m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = fp8_value(A[m * K + k], fmt) * fp8_value(B[n * K + k], fmt);
+                acc += p;
+                mag += fabs(p);
+            }
+            double c_in = (beta != 0.0) ? (double)Cin[m * N + n] : 0.0;
+            Cref[m * N + n] = scale * acc + beta * c_in;
+            den[m * N + n] = fabs(scale) * mag + fabs(beta * c_in) + 1e-30;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Fused Linear-layer epilogue on a GEMM result.
  *
  * A Linear layer computes Y = XW + b (page "From model computation to GPU

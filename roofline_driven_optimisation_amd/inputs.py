@@ -43,6 +43,46 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _fp8_table(fmt: int):
+    """(finite values ascending, their bytes) of an 8-bit float format from
+    its definition: fmt 0 E4M3 (bias 7, 3 mantissa bits, S.1111.111 NaN, no
+    infinity), fmt 1 E5M2 (bias 15, 2 mantissa bits, exponent 31 inf/NaN)."""
+    vals, codes = [], []
+    for b in range(256):
+        s = -1.0 if b & 0x80 else 1.0
+        if fmt == 0:
+            e, m = (b >> 3) & 15, b & 7
+            if e == 15 and m == 7:
+                continue
+            v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        else:
+            e, m = (b >> 2) & 31, b & 3
+            if e == 31:
+                continue
+            v = (m / 4.0) * 2.0 ** -14 if e == 0 else (1 + m / 4.0) * 2.0 ** (e - 15)
+        if v == 0.0 and s < 0:
+            continue  # one zero: +0
+        vals.append(s * v)
+        codes.append(b)
+    order = np.argsort(vals, kind="stable")
+    return np.array(vals)[order], np.array(codes, dtype=np.uint8)[order]
+
+
+def f32_to_fp8_bits(x: np.ndarray, fmt: int = 0) -> np.ndarray:
+    """Round float32 values to an 8-bit float format (nearest, ties to the
+    code with an even last mantissa bit; beyond the largest finite value,
+    saturate to it).  Returns the bytes as uint8."""
+    vals, codes = _fp8_table(fmt)
+    x = np.asarray(x, dtype=np.float64)
+    flat = np.clip(x.reshape(-1), vals[0], vals[-1])
+    hi = np.clip(np.searchsorted(vals, flat), 1, len(vals) - 1)
+    lo = hi - 1
+    dlo, dhi = flat - vals[lo], vals[hi] - flat
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((codes[hi] & 1) == 0))
+    out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    return out.reshape(x.shape)
+
+
 def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
     """One float32 matrix from a distribution spec.
 
