@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 4
+#define GEMM_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -151,6 +151,28 @@ GEMM_API int gemm_naive_f32(int M, int N, int K, float alpha, float beta,
                    const float *A, const float *B, float *C, void *stream);
 GEMM_API int gemm_naive_bf16(int M, int N, int K, float alpha, float beta,
                     const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/*
+ * 8-bit float GEMM: the smaller input type that raises the arithmetic
+ * intensity (page "Where kernel performance comes from", section on GEMM:
+ * one-byte operands move half the bytes of bf16 per multiply-add).
+ *
+ *     C = alpha * scale_a * scale_b * A * B^T + beta * C
+ *
+ * A is M x K and B is stored N x K (row n of B holds the K weights of
+ * output column n), both row-major bytes in `format`: GEMM_FP8_E4M3 (bias 7,
+ * 3 mantissa bits, largest 448, no infinity) or GEMM_FP8_E5M2 (bias 15, 2
+ * mantissa bits, largest 57344); scale_a and scale_b are per-tensor scales.
+ * Products are exact in fp32 and accumulate in fp32; C is float32 in and
+ * out.  K % 16 == 0 with 16-byte aligned A and B runs the matrix-core
+ * kernel (256 x 256 tiles, v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
+ * scales), anything else a one-thread-per-output kernel.  An unknown format
+ * and the gemm_bf16 argument errors return GEMM_ERR_INVALID_ARG.
+ */
+enum gemm_fp8_format { GEMM_FP8_E4M3 = 0, GEMM_FP8_E5M2 = 1 };
+GEMM_API int gemm_fp8(int M, int N, int K, float alpha, float beta, const uint8_t *A,
+                      const uint8_t *B, float *C, float scale_a, float scale_b, int format,
+                      void *stream);
 
 /*
  * Strided batched bf16 GEMM, the shape attention gives the GEMM: S = Q K^T

@@ -60,6 +60,8 @@ def library():
         lib.gemm_bf16_strided_batched.argtypes = [i, i, i, i, f, f, vp, ctypes.c_int64, vp,
                                                   ctypes.c_int64, i, vp, ctypes.c_int64, vp]
         lib.gemm_bf16_strided_batched.restype = ctypes.c_int
+        lib.gemm_fp8.argtypes = [i, i, i, f, f, vp, vp, vp, f, f, i, vp]
+        lib.gemm_fp8.restype = ctypes.c_int
         for name in ("reduce_sum_f32", "reduce_sum_f32_naive"):
             fn = getattr(lib, name)
             fn.argtypes = [vp, ctypes.c_int64, vp, vp]
@@ -204,6 +206,37 @@ def gemm_bf16_batched(A, B, C, alpha=1.0, beta=0.0, trans_b=False, stream=None):
             int(batch), int(M), int(N), int(K), float(alpha), float(beta),
             ctypes.c_void_p(A.data_ptr()), M * K, ctypes.c_void_p(B.data_ptr()), K * N,
             1 if trans_b else 0, ctypes.c_void_p(C.data_ptr()), M * N, _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
+    return C
+
+
+FP8_E4M3, FP8_E5M2 = 0, 1
+
+
+def gemm_fp8(A, B, C, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0, fmt=FP8_E4M3,
+             stream=None):
+    """C = alpha*scale_a*scale_b*A@B.T + beta*C with A (M x K) and B (N x K)
+    uint8 tensors of 8-bit float bytes (fmt E4M3 or E5M2), C float32."""
+    import torch
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 2-D tensor" % name)
+        if t.device.type != "cuda" or t.device != C.device:
+            raise ValueError("%s must be on C's GPU" % name)
+    if A.dtype != torch.uint8 or B.dtype != torch.uint8 or C.dtype != torch.float32:
+        raise TypeError("A and B must be uint8 and C float32")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    lib = library()
+    with torch.cuda.device(C.device):
+        status = lib.gemm_fp8(int(M), int(N), int(K), float(alpha), float(beta),
+                              ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()),
+                              ctypes.c_void_p(C.data_ptr()), float(scale_a), float(scale_b),
+                              int(fmt), _stream_handle(stream))
     if status != GEMM_OK:
         raise GemmError(status, _status_message(status))
     return C

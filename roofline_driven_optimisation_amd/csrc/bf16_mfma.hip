@@ -1266,6 +1266,197 @@ int tile_lds_bytes(int c) {
     return (c == 0 || c == 4) ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit float GEMM (E4M3 or E5M2 operands, fp32 accumulation), C = alpha A
+// B^T + beta C with B stored N x K: the four-wave 256 x 256 kernel's tile,
+// stages and copy pattern at one byte per element.  A K step is 64 elements
+// = 64 bytes per row, so the copies, the LDS layout (four 16-byte chunks per
+// row, chunk c of row r at c ^ ((r / 4) % 4)) and the LDS bytes read per
+// step are those of the bf16 kernel's 32-element step, and B's tile has A's
+// shape (no transposing reads).  v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// scales) takes from lane l the 32 bytes k = 32 (l / 32) .. + 31 of row
+// (l % 32) for both operands (checked on the device against a host
+// product); it does four times the work of the bf16 32x32x16 MFMA at the
+// 8-bit rate, so a step is 16 MFMAs per wave instead of 32.  Schedule: the
+// fragments of step t (two 16-byte reads each) are read while the last 8
+// MFMAs of step t - 1 run, the copies of step t + 3 go out with the first
+// 8 MFMAs of step t, then one wait and one barrier, as in the bf16 kernel.
+template <bool KTAIL, int FMT>
+__global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, float alpha,
+                                                        float beta,
+                                                        const uint8_t *__restrict__ A,
+                                                        const uint8_t *__restrict__ B, float *C,
+                                                        int tiles_m, int tiles_n) {
+    typedef int v8i __attribute__((ext_vector_type(8)));
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+    constexpr int BM = 256, BN = 256, S = 4, BK = 64;  // BK in elements = bytes
+    constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
+    constexpr int STAGE = BM * BK;                   // bytes, A and B alike
+    constexpr int LOADS = BM / 16 / 4;               // 1 KB copies per wave per operand
+    constexpr int COPIES = 2 * LOADS;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[S][STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[S][STAGE];
+
+    int tm, tn;
+    grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int T = (K + BK - 1) / BK;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // copies: lane p of a wave writes physical chunk p % 4 of row 16 wave +
+    // p / 4 (+ 64 q), holding logical chunk (p % 4) ^ ((p / 16) % 4)
+    const int row_in = lane >> 2;
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t off0 = static_cast<uint32_t>((16 * wave + row_in) * K + 16 * chunk);
+    const uint32_t step64 = static_cast<uint32_t>(64 * K);
+    struct StepCopy {
+        i32x4 ra, rb;
+        uint32_t la, lb;
+        bool ok;
+    };
+    auto step_copy = [&](int t) {
+        const int k0 = t * BK, stage = t % S;
+        StepCopy c;
+        c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                         static_cast<long long>(M - m0) * K - k0);
+        c.rb = make_desc(B + static_cast<size_t>(n0) * K + k0,
+                         static_cast<long long>(N - n0) * K - k0);
+        c.ok = !(KTAIL && k0 + 16 * chunk >= K);
+        c.la = lds_address(&lds_a[stage][wave * 1024]);
+        c.lb = lds_address(&lds_b[stage][wave * 1024]);
+        return c;
+    };
+    auto issue_copy = [&](const StepCopy &c, int q) {
+        const int r = q % LOADS;
+        if (q < LOADS)
+            lds_dma16(c.ra, c.la + r * 4096, c.ok ? off0 + r * step64 : kOOB);
+        else
+            lds_dma16(c.rb, c.lb + r * 4096, c.ok ? off0 + r * step64 : kOOB);
+    };
+
+    // fragment f of a step: f < MI is A block f, else B block f - MI; read
+    // order puts B block 0, the A blocks and B block 1 (what the first eight
+    // MFMAs use) first
+    const int swz = swz_a32(l32);
+    const int p0 = ((2 * h) ^ swz) * 16, p1 = ((2 * h + 1) ^ swz) * 16;
+    // each 32-byte fragment is filled by two 16-byte reads into its halves,
+    // so it is already one register tuple for the MFMA
+    u32x8 fa[2][MI], fb[2][NI];
+    auto load16 = [&](const uint8_t *row_base, int half) {
+        return *reinterpret_cast<const u32x4 *>(row_base + (half ? p1 : p0));
+    };
+    // fragment pair `o` (0 .. 7) of a step: B block 0, A blocks 0 .. 3,
+    // B blocks 1 .. 3 (the first eight MFMAs use B blocks 0 and 1)
+    auto read_pair = [&](int stage, int o, auto buf_tag) {
+        constexpr int buf = decltype(buf_tag)::value;
+        if (o >= 1 && o <= MI) {
+            const int i = o - 1;
+            const uint8_t *rb = &lds_a[stage][(wm * WM + 32 * i + l32) * BK];
+            fa[buf][i].lo = load16(rb, 0);
+            fa[buf][i].hi = load16(rb, 1);
+        } else {
+            const int jj = o == 0 ? 0 : o - MI;
+            const uint8_t *rb = &lds_b[stage][(wn * WN + 32 * jj + l32) * BK];
+            fb[buf][jj].lo = load16(rb, 0);
+            fb[buf][jj].hi = load16(rb, 1);
+        }
+    };
+    constexpr int kPairs = MI + NI;
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+    auto mfma = [&](int q, auto buf_tag) {  // B-major: consecutive MFMAs share B
+        constexpr int buf = decltype(buf_tag)::value;
+        const int jj = q / MI, i = q % MI;
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            __builtin_bit_cast(v8i, fb[buf][jj]), __builtin_bit_cast(v8i, fa[buf][i]), acc[i][jj],
+            FMT, FMT, 0, 127, 0, 127);
+    };
+    constexpr int kEarly = 8, kTail = 8;
+    constexpr int kWaitSteady = (2 * COPIES & 15) | (7 << 4) | ((2 * COPIES >> 4) << 14);
+    constexpr int kWaitDrain = (7 << 4);
+
+    for (int t = 0; t < S - 1; ++t)
+        if (t < T) {
+            const StepCopy c = step_copy(t);
+#pragma unroll
+            for (int q = 0; q < COPIES; ++q) issue_copy(c, q);
+        }
+    if (T >= S - 1)
+        __builtin_amdgcn_s_waitcnt(kWaitSteady);
+    else
+        __builtin_amdgcn_s_waitcnt(kWaitDrain);
+    __syncthreads();
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+#pragma unroll
+    for (int o = 0; o < kPairs; ++o) read_pair(0, o, Even());
+
+    // the fragment buffer is t % 2: each parity is compiled separately so
+    // that the fragment arrays are indexed statically (kept in registers)
+    const int copy_end = max(0, T - (S - 1));
+    auto k_step = [&](int t, auto buf_tag) {
+        const bool copy = t < copy_end;  // uniform
+        constexpr int buf = decltype(buf_tag)::value;
+        const int cur = t % S;
+        using Cur = std::integral_constant<int, buf>;
+        using Prev = std::integral_constant<int, buf ^ 1>;
+        if (t > 0) {
+#pragma unroll
+            for (int q = 0; q < kTail; ++q) {
+                mfma(kEarly + q, Prev());
+                read_pair(cur, q, Cur());
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        const StepCopy next = step_copy(copy ? t + S - 1 : t);
+#pragma unroll
+        for (int q = 0; q < kEarly; ++q) {
+            mfma(q, Cur());
+            if (copy) issue_copy(next, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (copy)
+            __builtin_amdgcn_s_waitcnt(kWaitSteady);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitDrain);
+        __syncthreads();
+    };
+    // two steps per iteration, so that each step's fragment buffer is fixed
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+        k_step(t, Even());
+        k_step(t + 1, Odd());
+    }
+    if (t < T) k_step(t, Even());
+    auto last = [&](auto buf_tag) {
+#pragma unroll
+        for (int q = 0; q < kTail; ++q) {
+            mfma(kEarly + q, buf_tag);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if ((T - 1) & 1) last(Odd());
+    else last(Even());
+
+    // epilogue: as the bf16 kernel's, each wave staging through a private
+    // 16 KB slice of the A stages
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + static_cast<size_t>(m0) * N + n0,
+                  (static_cast<long long>(M - m0) * N - n0) * 4);
+    static_assert(S * STAGE >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
+    float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
+    store_c_tile_lds128<MI>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta, rc, 0);
+}
+
 // Calls f(ktail, epi) with the two flags as std::integral_constant values, so
 // that a launcher can pick one of its four kernel instantiations.
 template <class F>
@@ -1405,6 +1596,25 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
         }
     }
     return best;
+}
+
+hipError_t launch_fp8_gemm(int M, int N, int K, float alpha, float beta, const uint8_t *A,
+                           const uint8_t *B, float *C, int fmt, hipStream_t stream) {
+    const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL || (fmt != 0 && fmt != 1) || K % 16 != 0)
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    const bool ktail = K % 64 != 0;
+    const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+    if (fmt == 0) {
+        if (ktail) fp8_q4_kernel<true, 0><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
+        else fp8_q4_kernel<false, 0><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
+    } else {
+        if (ktail) fp8_q4_kernel<true, 1><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
+        else fp8_q4_kernel<false, 1><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,

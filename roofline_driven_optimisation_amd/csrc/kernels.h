@@ -96,6 +96,15 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
                                const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
                                bool trans_b, hipStream_t stream);
+// 8-bit float GEMM, C = alpha A B^T + beta C with B stored N x K: fmt 0
+// E4M3, 1 E5M2 (both operands).  Needs K % 16 == 0, 16-byte aligned A and
+// B, K <= 2^21 and N <= 2^20.
+hipError_t launch_fp8_gemm(int M, int N, int K, float alpha, float beta, const uint8_t *A,
+                           const uint8_t *B, float *C, int fmt, hipStream_t stream);
+// One thread per output element for any 8-bit float shape or alignment.
+hipError_t launch_naive_fp8(int M, int N, int K, float alpha, float beta, const uint8_t *A,
+                            const uint8_t *B, float *C, int fmt, hipStream_t stream);
+
 // One thread per output element, any layout: the batched fallback.
 hipError_t launch_naive_bf16_batched(int M, int N, int K, float alpha, float beta,
                                      const uint16_t *A, const uint16_t *B, float *C,

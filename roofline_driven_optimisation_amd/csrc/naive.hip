@@ -40,6 +40,44 @@ __global__ __launch_bounds__(256) void naive_kernel(int M, int N, int K, float a
     C[idx] = epi_apply<EPI>(out, EPI && epi.bias ? epi.bias[col] : 0.0f, epi.act);
 }
 
+// An 8-bit float byte as fp32, from the format definitions: fmt 0 E4M3
+// (bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, S.1111.111 NaN, no
+// infinity), fmt 1 E5M2 (bias 15, 2 mantissa bits, subnormals m/4 * 2^-14,
+// exponent 31 infinity or NaN).  Every value is exact in fp32.
+__device__ __forceinline__ float fp8_to_float(uint8_t b, int fmt) {
+    const bool neg = (b & 0x80u) != 0;
+    float v;
+    if (fmt == 0) {
+        const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+        if (e == 15u && m == 7u) return __builtin_nanf("");
+        v = e == 0u ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    } else {
+        const uint32_t e = (b >> 2) & 31u, m = b & 3u;
+        if (e == 31u) return m == 0u ? (neg ? -__builtin_inff() : __builtin_inff()) : __builtin_nanf("");
+        v = e == 0u ? static_cast<float>(m) * 0x1p-16f : __uint_as_float(((e + 112u) << 23) | (m << 21));
+    }
+    return neg ? -v : v;
+}
+
+// The 8-bit float fallback: one thread per output, B stored N x K.
+__global__ __launch_bounds__(256) void naive_fp8_kernel(int M, int N, int K, float alpha,
+                                                        float beta, const uint8_t *A,
+                                                        const uint8_t *B, float *C, int tiles_n,
+                                                        int fmt) {
+    const int tile = blockIdx.x;
+    const int row = (tile / tiles_n) * 16 + threadIdx.y;
+    const int col = (tile % tiles_n) * 16 + threadIdx.x;
+    if (row >= M || col >= N) return;
+    const uint8_t *a = A + static_cast<size_t>(row) * K;
+    const uint8_t *b = B + static_cast<size_t>(col) * K;
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum = fmaf(fp8_to_float(a[k], fmt), fp8_to_float(b[k], fmt), sum);
+    const size_t idx = static_cast<size_t>(row) * N + col;
+    float out = alpha * sum;
+    if (beta != 0.0f) out = fmaf(beta, C[idx], out);
+    C[idx] = out;
+}
+
 // The batched fallback: item blockIdx.y, B stored K x N, or N x K with TRANSB.
 template <bool TRANSB>
 __global__ __launch_bounds__(256) void naive_batched_kernel(int M, int N, int K, float alpha,
@@ -124,6 +162,16 @@ hipError_t launch_naive_bf16_batched(int M, int N, int K, float alpha, float bet
     else
         naive_batched_kernel<false><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
                                                                 static_cast<int>(tiles_n), batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive_fp8(int M, int N, int K, float alpha, float beta, const uint8_t *A,
+                            const uint8_t *B, float *C, int fmt, hipStream_t stream) {
+    const long long tiles_m = (M + 15) / 16, tiles_n = (N + 15) / 16;
+    const long long tiles = tiles_m * tiles_n;
+    if (tiles > 0x7fffffffLL || (fmt != 0 && fmt != 1)) return hipErrorInvalidValue;
+    naive_fp8_kernel<<<dim3(static_cast<unsigned>(tiles)), dim3(16, 16), 0, stream>>>(
+        M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_n), fmt);
     return hipGetLastError();
 }
 

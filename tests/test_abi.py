@@ -33,7 +33,7 @@ def test_header_declares_expected_api():
     names = declared_functions()
     for n in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16",
               "gemm_f32_bias_act", "gemm_bf16_bias_act", "reduce_sum_f32", "reduce_sum_f32_naive",
-              "gemm_bf16_strided_batched",
+              "gemm_bf16_strided_batched", "gemm_fp8",
               "gemm_status_string", "gemm_last_kernel", "gemm_abi_version"):
         assert n in names
 

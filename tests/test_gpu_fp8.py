@@ -1,0 +1,155 @@
+"""GPU parity of the 8-bit float GEMM (E4M3 and E5M2, B stored N x K, fp32
+C) through the C ABI, against the oracle: the matrix-core kernel (full K
+steps and a K tail, ragged M and N, per-tensor scales, beta), the
+one-thread-per-output fallback (K not a multiple of 16, unaligned operands),
+K = 0, exact on integer inputs, within the fp32-accumulation tolerance on
+random inputs and on every finite code (subnormals and the largest values
+included), and at 4096 x 4096 x 4096 on a sampled 64 x 64 block."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL, log
+from roofline_driven_optimisation_amd import binding
+from roofline_driven_optimisation_amd.inputs import _fp8_table, f32_to_fp8_bits
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [0, 1]
+FMT_ID = ["e4m3", "e5m2"]
+
+
+def draw(M, N, K, fmt, dist, seed):
+    rng = np.random.default_rng(seed)
+    if dist == "int":
+        a = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+        b = rng.integers(-4, 5, size=(N, K)).astype(np.float32)
+    elif dist == "codes":  # every finite code, uniformly
+        _, codes = _fp8_table(fmt)
+        return (rng.choice(codes, size=(M, K)).astype(np.uint8),
+                rng.choice(codes, size=(N, K)).astype(np.uint8), rng)
+    else:
+        a = rng.standard_normal((M, K)).astype(np.float32)
+        b = (rng.standard_normal((N, K)) * 0.5).astype(np.float32)
+    return f32_to_fp8_bits(a, fmt), f32_to_fp8_bits(b, fmt), rng
+
+
+def run(A, B, C, alpha, beta, sa, sb, fmt, offset=0):
+    """C on the GPU; ``offset`` > 0 places A and B that many bytes past a
+    16-byte boundary."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+
+    def dev(x):
+        buf = torch.zeros(x.size + offset, dtype=torch.uint8, device="cuda")
+        t = buf[offset:].view(x.shape)
+        t.copy_(torch.from_numpy(x))
+        return t
+
+    At, Bt = dev(A), dev(B)
+    Ct = (torch.from_numpy(C).cuda() if C is not None
+          else torch.full((M, N), float("nan"), device="cuda"))
+    log("  gpu fp8 fmt=%d %dx%dx%d alpha=%g beta=%g sa=%g sb=%g offset=%d" % (
+        fmt, M, N, K, alpha, beta, sa, sb, offset))
+    binding.gemm_fp8(At, Bt, Ct, alpha, beta, sa, sb, fmt)
+    name = binding.last_kernel()
+    torch.cuda.synchronize()
+    return Ct.cpu().numpy(), name
+
+
+CASES = [  # (M, N, K, offset, expected kernel)
+    (256, 256, 64, 0, "fp8_q4_256x256x64"),
+    (300, 520, 256, 0, "fp8_q4_256x256x64"),
+    (300, 520, 144, 0, "fp8_q4_256x256x64"),      # K tail of 16
+    (520, 300, 1072, 0, "fp8_q4_256x256x64"),     # K tail of 48, several steps
+    (37, 600, 16, 0, "fp8_q4_256x256x64"),        # one partial K step
+    (1, 1000, 512, 0, "fp8_q4_256x256x64"),
+    (70, 90, 60, 0, "naive_fp8"),                 # K % 16 != 0
+    (70, 90, 64, 1, "naive_fp8"),                 # unaligned A and B
+]
+
+
+def ids(c):
+    return "%dx%dx%d%s" % (c[0], c[1], c[2], "_off" if c[3] else "")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_fp8_exact_integers(case, fmt):
+    M, N, K, offset, want = case
+    A, B, rng = draw(M, N, K, fmt, "int", seed=M + N + K)
+    C = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
+    got, name = run(A, B, C, 1.0, 0.5, 1.0, 2.0, fmt, offset)
+    assert name == want, name
+    ref, _ = oracle.gemm_fp8(A, B, C, 1.0, 0.5, 1.0, 2.0, fmt)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
+@pytest.mark.parametrize("case", CASES, ids=ids)
+def test_fp8_random(case, fmt):
+    M, N, K, offset, want = case
+    A, B, _ = draw(M, N, K, fmt, "n", seed=7 + K)
+    got, name = run(A, B, None, 1.25, 0.0, 0.5, 0.125, fmt, offset)
+    assert name == want, name
+    ref, den = oracle.gemm_fp8(A, B, None, 1.25, 0.0, 0.5, 0.125, fmt)
+    err = oracle.parity_error(got, ref, den)
+    log("  fp8 parity err=%.3e" % err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
+@pytest.mark.parametrize("offset", [0, 1], ids=["mfma", "naive"])
+def test_fp8_every_finite_code(fmt, offset):
+    """Operands drawn from every finite code of the format: subnormals,
+    both zeros' neighbours and the largest magnitudes (448 and 57344)."""
+    M, N, K = 264, 288, 320
+    A, B, _ = draw(M, N, K, fmt, "codes", seed=11 + fmt)
+    got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt, offset)
+    assert name == ("naive_fp8" if offset else "fp8_q4_256x256x64"), name
+    ref, den = oracle.gemm_fp8(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
+    err = oracle.parity_error(got, ref, den)
+    log("  fp8 all-codes err=%.3e" % err)
+    assert err <= TOL["bf16"]
+
+
+def test_fp8_k_zero():
+    A = np.zeros((40, 0), np.uint8)
+    B = np.zeros((72, 0), np.uint8)
+    C = np.random.default_rng(1).integers(-4, 5, size=(40, 72)).astype(np.float32)
+    got, name = run(A, B, C, 1.0, 0.5, 1.0, 1.0, 0)
+    assert name == "scale_c", name
+    assert np.array_equal(got, C * 0.5)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
+def test_fp8_full_size_sampled(fmt):
+    """4096 x 4096 x 4096, the size the throughput is measured at: a 64 x 64
+    block of sampled rows and columns against the oracle's sub-GEMM."""
+    M = N = K = 4096
+    A, B, rng = draw(M, N, K, fmt, "n", seed=5)
+    got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
+    assert name == "fp8_q4_256x256x64", name
+    rows = np.sort(rng.choice(M, 64, replace=False))
+    cols = np.sort(rng.choice(N, 64, replace=False))
+    ref, den = oracle.gemm_fp8(A[rows], B[cols], None, 1.0, 0.0, 1.0, 1.0, fmt)
+    err = oracle.parity_error(got[np.ix_(rows, cols)], ref, den)
+    log("  fp8 4096 sampled err=%.3e" % err)
+    assert err <= TOL["bf16"]
+
+
+def test_fp8_bad_arguments():
+    import torch
+    lib = binding.library()
+    x = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    c = torch.zeros(4096, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    assert lib.gemm_fp8(8, 8, 16, 1.0, 0.0, p(x), p(x), p(c), 1.0, 1.0, 2, s) == 1
+    assert lib.gemm_fp8(-1, 8, 16, 1.0, 0.0, p(x), p(x), p(c), 1.0, 1.0, 0, s) == 1
+    assert lib.gemm_fp8(8, 8, 16, 1.0, 0.0, None, p(x), p(c), 1.0, 1.0, 0, s) == 1
+    assert lib.gemm_fp8(0, 8, 16, 1.0, 0.0, p(x), p(x), p(c), 1.0, 1.0, 0, s) == 0
+    torch.cuda.synchronize()
