@@ -11,8 +11,10 @@ by device synchronisations.  The same line carries:
   stream) against the bf16 MFMA peak, plus HBM traffic from rocprofv3
   counters when a counter summary for the current kernel source exists;
 * ``also``: the other workloads (fp32 4096^3 and 4092^3 with alpha 1.5 and
-  beta 0.5, LLaMA-7B prefill projections, decode-shaped GEMMs) with TFLOP/s,
-  algorithmic GB/s and their own roofline fraction;
+  beta 0.5, LLaMA-7B prefill projections, decode-shaped GEMMs, the fused
+  bias + activation epilogue, the 10^8-float vector sum, attention's batched
+  QK^T and PV, 8-bit float GEMMs) with TFLOP/s, algorithmic GB/s and their
+  own roofline fraction;
 * ``ladder``: the one-thread-per-output kernel against the tiled one on
   fp32 4092^3, the first and last rungs of the optimisation ladder;
 * ``page_context``: the figures the pages quote for other machines;
@@ -48,7 +50,7 @@ SECONDARY = ["f32_4096", "f32_4092", "prefill_qkv", "prefill_o", "prefill_gate_u
              "prefill_down", "decode_up_m1", "decode_up_m8", "decode_up_m16",
              "decode_down_m1", "decode_down_m8", "decode_down_m16", "decode_lm_head",
              "prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu", "sum_1e8",
-             "attn_qk", "attn_pv"]
+             "attn_qk", "attn_pv", "fp8_4096", "fp8_prefill_gate_up"]
 # "<workload>+bias_<act>": the workload through the fused Linear-layer
 # epilogue, C = act(A*B + bias) with a normal(0, 0.5) bias over the columns
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
@@ -203,7 +205,44 @@ class PreparedBatched:
         return binding.last_kernel()
 
 
+# 8-bit float GEMMs (E4M3 operands, B stored N x K, fp32 C, beta = 0):
+# name -> (M, N, K)
+FP8 = {"fp8_4096": (4096, 4096, 4096), "fp8_prefill_gate_up": (2048, 11008, 4096)}
+
+
+class PreparedFp8:
+    """8-bit float GEMM: A ~ normal(0, 1) and B ~ normal(0, 0.02) (seed 0)
+    rounded to E4M3, per-tensor scales 1, rotated across copies."""
+
+    def __init__(self, name: str, seed: int = 0):
+        import torch
+        from roofline_driven_optimisation_amd.inputs import f32_to_fp8_bits
+        self.name = name
+        self.M, self.N, self.K = FP8[name]
+        rng = np.random.default_rng(seed)
+        a = f32_to_fp8_bits(rng.standard_normal((self.M, self.K)).astype(np.float32), 0)
+        b = f32_to_fp8_bits((rng.standard_normal((self.N, self.K)) * 0.02).astype(np.float32), 0)
+        A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+        C = torch.zeros(self.M, self.N, dtype=torch.float32, device="cuda")
+        per_set = A.numel() + B.numel() + 4 * C.numel()
+        self.sets = max(1, -(-ROTATE_BYTES // per_set))
+        self.bufs = [(A, B, C)] + [(A.clone(), B.clone(), C.clone()) for _ in range(self.sets - 1)]
+        self.rf = rl.gemm_roofline(self.M, self.N, self.K, "fp8", False)
+
+    def launch(self, i: int, naive: bool = False):
+        from roofline_driven_optimisation_amd import binding
+        A, B, C = self.bufs[i % self.sets]
+        binding.gemm_fp8(A, B, C, 1.0, 0.0, fmt=binding.FP8_E4M3)
+
+    def kernel_name(self) -> str:
+        from roofline_driven_optimisation_amd import binding
+        self.launch(0)
+        return binding.last_kernel()
+
+
 def prepare(name: str):
+    if name in FP8:
+        return PreparedFp8(name)
     if name.startswith("sum_"):
         return PreparedSum(name)
     if name in ATTENTION:
@@ -250,6 +289,11 @@ def summary(p, sec: float, kname: str) -> dict:
     if isinstance(p, PreparedSum):
         return {"workload": p.name, "n": p.n, "dtype": "f32", "kernel": kname,
                 "us": round(sec * 1e6, 2), "gbs": round(gbs, 1), "bound": p.rf.bound,
+                "frac": round(p.rf.fraction(sec), 4)}
+    if isinstance(p, PreparedFp8):
+        return {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "dtype": "fp8_e4m3",
+                "kernel": kname, "us": round(sec * 1e6, 2), "tflops": round(tflops, 2),
+                "bound": p.rf.bound, "roofline_tflops": round(p.rf.attainable / 1e12, 1),
                 "frac": round(p.rf.fraction(sec), 4)}
     if isinstance(p, PreparedBatched):
         return {"workload": p.name, "batch": p.batch, "M": p.M, "N": p.N, "K": p.K,

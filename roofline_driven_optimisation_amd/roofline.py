@@ -16,7 +16,8 @@ The model is the one the pages build up:
   which drops the C read when beta = 0).
 
 MI355X peaks are AMD's published figures, not the pages': dense bf16 MFMA
-2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP per CU per clock), fp32
+2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP per CU per clock), fp8 twice
+that (5033 TFLOP/s), fp32
 157.3 TFLOP/s, HBM3E 8.0 TB/s.
 """
 from __future__ import annotations
@@ -28,6 +29,7 @@ MI355X_CUS = 256
 MI355X_CLOCK_HZ = 2.4e9
 MI355X_BF16_FLOP_PER_CLK_PER_CU = 4096
 MI355X_PEAK_BF16 = MI355X_CUS * MI355X_CLOCK_HZ * MI355X_BF16_FLOP_PER_CLK_PER_CU  # 2.5166e15
+MI355X_PEAK_FP8 = 2 * MI355X_PEAK_BF16  # 8-bit float MFMA: twice the bf16 rate
 MI355X_PEAK_FP32 = 157.3e12
 MI355X_PEAK_HBM = 8.0e12  # bytes/s
 
@@ -120,7 +122,7 @@ class Roofline:
     ai: float
     peak_compute: float
     peak_bw: float
-    bound: str  # "mfma" (bf16 matrix cores), "fp32" (fp32 compute) or "hbm"
+    bound: str  # "mfma" (bf16 or fp8 matrix cores), "fp32" (fp32 compute) or "hbm"
     attainable: float
 
     def fraction(self, seconds: float) -> float:
@@ -139,13 +141,13 @@ def gemm_roofline(M: int, N: int, K: int, dtype: str, beta_nonzero: bool,
     in_bytes = ELEM_BYTES[dtype]
     flops = gemm_flops(M, N, K)
     nbytes = gemm_bytes(M, N, K, in_bytes, 4, beta_nonzero) + (4 * N if bias else 0)
-    peak = MI355X_PEAK_BF16 if dtype == "bf16" else MI355X_PEAK_FP32
+    peak = {"bf16": MI355X_PEAK_BF16, "fp8": MI355X_PEAK_FP8}.get(dtype, MI355X_PEAK_FP32)
     ai = flops / nbytes
     att = attainable(peak, MI355X_PEAK_HBM, ai)
     if MI355X_PEAK_HBM * ai < peak:
         bound = "hbm"
     else:
-        bound = "mfma" if dtype == "bf16" else "fp32"
+        bound = "mfma" if dtype in ("bf16", "fp8") else "fp32"
     return Roofline(flops, nbytes, ai, peak, MI355X_PEAK_HBM, bound, att)
 
 
