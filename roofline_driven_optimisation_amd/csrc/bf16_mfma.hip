@@ -928,6 +928,92 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
             acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
 }
 
+// Tile and K half of workgroup `bid` under a split plan: workgroups below
+// split_from own a whole tile (XCD-aware order, split = -1); the rest come
+// in pairs that share a tile, split 0 taking the K steps before split_step
+// and split 1 the others.  With xcd_pairs, workgroups b and b + 8 pair up
+// (one XCD under round-robin dealing), else 2i and 2i + 1.
+__device__ __forceinline__ void split_tile(int bid, const PPSplit &plan, int &v, int &split) {
+    split = -1;
+    if (bid < plan.split_from) {
+        v = xcd_remap(bid, plan.split_from);
+    } else if (plan.xcd_pairs) {
+        const int q = bid - plan.split_from;
+        const int p = (q >> 4) * 8 + (q & 7);
+        v = plan.split_from + xcd_remap(p, plan.grid_tiles - plan.split_from);
+        split = (q >> 3) & 1;
+    } else {
+        const int q = bid - plan.split_from;
+        v = plan.split_from + (q >> 1);
+        split = q & 1;
+    }
+}
+
+// The epilogue of a 256 x 256 four-wave tile under a split plan: a whole
+// tile stores alpha acc + beta C; the first of a split pair posts its
+// partial to the pair's workspace slot and raises the slot's flag; the
+// second waits for the flag (a bounded poll: on time-out it writes NaN
+// rather than hang) and stores alpha (acc + partial) + beta C.  Flag
+// accesses are device-scope for pairs on one XCD, system scope through
+// uncached memory otherwise.
+template <int MI, bool EPI>
+__device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], float *region,
+                                                 __amdgpu_buffer_rsrc_t rc, int row0, int col0,
+                                                 int cols_left, int N, float alpha, float beta,
+                                                 int split, int v, const PPSplit &split_plan,
+                                                 const float *bias, int act) {
+    constexpr int BN = kPPTile;
+    const int tid = threadIdx.x;
+    if (split < 0) {
+        store_c_tile_lds128<MI, kStoreC, kSystemScope, EPI>(acc, region, rc, row0, col0,
+                                                            cols_left, N, alpha, beta, rc, 0,
+                                                            bias, act);
+        return;
+    }
+    const int slot = v - split_plan.split_from;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BN * BN, BN * BN * 4);
+    int *flag = split_plan.flags + slot;
+    const bool local = split_plan.xcd_pairs != 0;
+    if (split == 0) {
+        store_c_tile_lds128<MI, kPostPartial>(acc, region, rc, row0, col0, cols_left, N, alpha,
+                                              beta, rw, BN);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+        __syncthreads();
+        if (tid == 0) {
+            if (local)
+                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        return;
+    }
+    __shared__ int s_ready;
+    if (tid == 0) {
+        int ready = 0;
+        for (int poll = 0; poll < (1 << 22); ++poll) {
+            const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (f == split_plan.epoch) {
+                ready = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        s_ready = ready;
+    }
+    __syncthreads();
+    const float a = s_ready ? alpha : __builtin_nanf("");
+    if (local)
+        store_c_tile_lds128<MI, kAddPartial, kDeviceScope, EPI>(
+            acc, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
+    else
+        store_c_tile_lds128<MI, kAddPartial, kSystemScope, EPI>(
+            acc, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
+}
+
 // ---------------------------------------------------------------------------
 // Four-wave 256 x 256 kernel on the ping-pong kernel's 32-k LDS layout:
 // 256 threads = four waves in 2 x 2, each owning a 128 x 128 wave tile (256
@@ -979,20 +1065,8 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     // Tile and K range: as in the ping-pong kernel, workgroups below
     // split_from own a whole tile (XCD-aware order) and the rest come in
     // pairs that share a tile, one per half of the K steps.
-    const int bid = blockIdx.x;
-    int v, split = -1;
-    if (bid < split_plan.split_from) {
-        v = xcd_remap(bid, split_plan.split_from);
-    } else if (split_plan.xcd_pairs) {
-        const int q = bid - split_plan.split_from;
-        const int p = (q >> 4) * 8 + (q & 7);
-        v = split_plan.split_from + xcd_remap(p, (split_plan.grid_tiles - split_plan.split_from));
-        split = (q >> 3) & 1;
-    } else {
-        const int q = bid - split_plan.split_from;
-        v = split_plan.split_from + (q >> 1);
-        split = q & 1;
-    }
+    int v, split;
+    split_tile(blockIdx.x, split_plan, v, split);
     // A batched launch (never split) numbers the tiles of all items in
     // turn: the XCD-aware order keeps one item's tiles on one XCD.
     const int per_item = tiles_m * tiles_n;
@@ -1192,56 +1266,8 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
     const int row0 = wm * WM, col0 = wn * WN;
     const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
-    if (split < 0) {
-        store_c_tile_lds128<MI, kStoreC, kSystemScope, EPI>(acc, region, rc, row0, col0, N - n0,
-                                                            N, alpha, beta, rc, 0, bias, epi.act);
-        return;
-    }
-    // A split tile: the partial lives in the workspace slot of the pair; the
-    // handshake is the ping-pong kernel's (device-scope flag accesses for
-    // pairs on one XCD, system scope through uncached memory otherwise).
-    const int slot = v - split_plan.split_from;
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BM * BN, BM * BN * 4);
-    int *flag = split_plan.flags + slot;
-    const bool local = split_plan.xcd_pairs != 0;
-    if (split == 0) {
-        store_c_tile_lds128<MI, kPostPartial>(acc, region, rc, row0, col0, N - n0, N, alpha,
-                                              beta, rw, BN);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
-        __syncthreads();
-        if (tid == 0) {
-            if (local)
-                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            else
-                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-        return;
-    }
-    __shared__ int s_ready;
-    if (tid == 0) {
-        int ready = 0;
-        for (int poll = 0; poll < (1 << 22); ++poll) {
-            const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            if (f == split_plan.epoch) {
-                ready = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        s_ready = ready;
-    }
-    __syncthreads();
-    const float a = s_ready ? alpha : __builtin_nanf("");
-    if (local)
-        store_c_tile_lds128<MI, kAddPartial, kDeviceScope, EPI>(
-            acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
-    else
-        store_c_tile_lds128<MI, kAddPartial, kSystemScope, EPI>(
-            acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
+    store_split_tile<MI, EPI>(acc, region, rc, row0, col0, N - n0, N, alpha, beta, split, v,
+                              split_plan, bias, epi.act);
 }
 
 
@@ -1286,10 +1312,11 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
                                                         float beta,
                                                         const uint8_t *__restrict__ A,
                                                         const uint8_t *__restrict__ B, float *C,
-                                                        int tiles_m, int tiles_n) {
+                                                        int tiles_m, int tiles_n,
+                                                        PPSplit split_plan) {
     typedef int v8i __attribute__((ext_vector_type(8)));
     typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-    constexpr int BM = 256, BN = 256, S = 4, BK = 64;  // BK in elements = bytes
+    constexpr int BM = 256, BN = 256, S = 4, BK = kFp8BK;  // BK in elements = bytes
     constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
     constexpr int STAGE = BM * BK;                   // bytes, A and B alike
     constexpr int LOADS = BM / 16 / 4;               // 1 KB copies per wave per operand
@@ -1297,10 +1324,16 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[S][STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[S][STAGE];
 
+    // tile and K range under the split plan (as the bf16 four-wave kernel)
+    int v, split;
+    split_tile(blockIdx.x, split_plan, v, split);
     int tm, tn;
-    grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, 4, tm, tn);
+    grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int T = (K + BK - 1) / BK;
+    const int total_steps = (K + BK - 1) / BK;
+    const int t_begin = split == 1 ? split_plan.split_step : 0;
+    const int t_end = split == 0 ? split_plan.split_step : total_steps;
+    const int T = t_end - t_begin;  // this workgroup's steps; t below counts them
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -1318,7 +1351,7 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
         bool ok;
     };
     auto step_copy = [&](int t) {
-        const int k0 = t * BK, stage = t % S;
+        const int k0 = (t_begin + t) * BK, stage = t % S;
         StepCopy c;
         c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
                          static_cast<long long>(M - m0) * K - k0);
@@ -1454,7 +1487,8 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
                   (static_cast<long long>(M - m0) * N - n0) * 4);
     static_assert(S * STAGE >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
-    store_c_tile_lds128<MI>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta, rc, 0);
+    store_split_tile<MI, false>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta, split,
+                                v, split_plan, nullptr, kActNone);
 }
 
 // Calls f(ktail, epi) with the two flags as std::integral_constant values, so
@@ -1472,10 +1506,10 @@ void with_flags(bool ktail, bool epi, F &&f) {
 
 // Checks a split plan against the tile count and K; fills `plan` (whole
 // tiles only when split is null).
-bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan) {
+bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan, int bk = kPPBK) {
     plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
     if (split == nullptr) return true;
-    const int steps = (K + kPPBK - 1) / kPPBK;
+    const int steps = (K + bk - 1) / bk;
     if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
         split->split_step >= steps ||
         (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
@@ -1599,22 +1633,43 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
 }
 
 hipError_t launch_fp8_gemm(int M, int N, int K, float alpha, float beta, const uint8_t *A,
-                           const uint8_t *B, float *C, int fmt, hipStream_t stream) {
+                           const uint8_t *B, float *C, int fmt, const PPSplit *split,
+                           hipStream_t stream) {
     const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const long long tiles = tiles_m * tiles_n;
-    if (tiles > 0x7fffffffLL || (fmt != 0 && fmt != 1) || K % 16 != 0)
+    if (tiles > 0x3fffffffLL || (fmt != 0 && fmt != 1) || K % 16 != 0)
         return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
-    const bool ktail = K % 64 != 0;
+    PPSplit plan;
+    if (!make_plan(split, tiles, K, plan, kFp8BK)) return hipErrorInvalidValue;
+    const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
+    const dim3 g(static_cast<unsigned>(grid)), block(kThreads);
+    const bool ktail = K % kFp8BK != 0;
     const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+    auto go = [&](auto kt, auto f) {
+        fp8_q4_kernel<decltype(kt)::value, decltype(f)::value>
+            <<<g, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn, plan);
+    };
+    using F0 = std::integral_constant<int, 0>;
+    using F1 = std::integral_constant<int, 1>;
     if (fmt == 0) {
-        if (ktail) fp8_q4_kernel<true, 0><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
-        else fp8_q4_kernel<false, 0><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
+        if (ktail) go(std::true_type(), F0());
+        else go(std::false_type(), F0());
     } else {
-        if (ktail) fp8_q4_kernel<true, 1><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
-        else fp8_q4_kernel<false, 1><<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn);
+        if (ktail) go(std::true_type(), F1());
+        else go(std::false_type(), F1());
     }
     return hipGetLastError();
+}
+
+int fp8_split_tiles(int M, int N, int K, int num_cus) {
+    // as for bf16: split the last round when it is at most half full and
+    // each half keeps at least four 64-deep K steps
+    const long long tiles =
+        static_cast<long long>((M + kPPTile - 1) / kPPTile) * ((N + kPPTile - 1) / kPPTile);
+    const long long r = num_cus > 0 ? tiles % num_cus : 0;
+    const int steps = (K + kFp8BK - 1) / kFp8BK;
+    if (r == 0 || 2 * r > num_cus || steps < 8) return 0;
+    return static_cast<int>(r);
 }
 
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,

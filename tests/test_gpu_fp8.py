@@ -64,9 +64,11 @@ CASES = [  # (M, N, K, offset, expected kernel)
     (256, 256, 64, 0, "fp8_q4_256x256x64"),
     (300, 520, 256, 0, "fp8_q4_256x256x64"),
     (300, 520, 144, 0, "fp8_q4_256x256x64"),      # K tail of 16
-    (520, 300, 1072, 0, "fp8_q4_256x256x64"),     # K tail of 48, several steps
-    (37, 600, 16, 0, "fp8_q4_256x256x64"),        # one partial K step
-    (1, 1000, 512, 0, "fp8_q4_256x256x64"),
+    (520, 300, 1072, 0, "fp8_q4_256x256x64_splitk"),      # K tail of 48, split pairs
+    (37, 600, 16, 0, "fp8_q4_256x256x64"),               # one partial K step
+    (1, 1000, 512, 0, "fp8_q4_256x256x64_splitk"),
+    (1024, 512, 1024, 0, "fp8_q4_256x256x64_splitk_xcd"),  # 8 split tiles: pairs on one XCD
+    (1040, 520, 1104, 0, "fp8_q4_256x256x64_splitk"),     # 15 split tiles, K tail of 16
     (70, 90, 60, 0, "naive_fp8"),                 # K % 16 != 0
     (70, 90, 64, 1, "naive_fp8"),                 # unaligned A and B
 ]
@@ -116,6 +118,21 @@ def test_fp8_every_finite_code(fmt, offset):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("shape", [(520, 300, 1072), (1024, 512, 1024)], ids=["pairs", "xcd"])
+def test_fp8_split_repeats(shape):
+    """Split tiles exchange partials through flags with a fresh epoch per
+    call: three calls in a row give the same bits, equal to the oracle on
+    integers."""
+    M, N, K = shape
+    A, B, rng = draw(M, N, K, 0, "int", seed=21)
+    C = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
+    ref, _ = oracle.gemm_fp8(A, B, C, 1.0, 0.5, 1.0, 1.0, 0)
+    for _ in range(3):
+        got, name = run(A, B, C, 1.0, 0.5, 1.0, 1.0, 0)
+        assert "splitk" in name, name
+        assert np.array_equal(got.astype(np.float64), ref)
+
+
 def test_fp8_k_zero():
     A = np.zeros((40, 0), np.uint8)
     B = np.zeros((72, 0), np.uint8)
@@ -125,14 +142,20 @@ def test_fp8_k_zero():
     assert np.array_equal(got, C * 0.5)
 
 
+FULL = [(4096, 4096, 4096, "fp8_q4_256x256x64"),
+        (2048, 11008, 4096, "fp8_q4_256x256x64_splitk_xcd")]
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
-def test_fp8_full_size_sampled(fmt):
-    """4096 x 4096 x 4096, the size the throughput is measured at: a 64 x 64
-    block of sampled rows and columns against the oracle's sub-GEMM."""
-    M = N = K = 4096
+@pytest.mark.parametrize("shape", FULL, ids=lambda c: "%dx%dx%d" % c[:3])
+def test_fp8_full_size_sampled(shape, fmt):
+    """The sizes the throughput is measured at (4096^3; 2048 x 11008 x 4096,
+    whose third-full last round is split over K): a 64 x 64 block of sampled
+    rows and columns against the oracle's sub-GEMM."""
+    M, N, K, want = shape
     A, B, rng = draw(M, N, K, fmt, "n", seed=5)
     got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
-    assert name == "fp8_q4_256x256x64", name
+    assert name == want, name
     rows = np.sort(rng.choice(M, 64, replace=False))
     cols = np.sort(rng.choice(N, 64, replace=False))
     ref, den = oracle.gemm_fp8(A[rows], B[cols], None, 1.0, 0.0, 1.0, 1.0, fmt)
