@@ -398,7 +398,7 @@ def sustain(name: str, seconds: float) -> dict:
     clock and board power (steady state: power- and thermally-settled)."""
     import threading
     import torch
-    p = Prepared(name)
+    p = prepare(name)
     kname = p.kernel_name()
     samples = []
 

@@ -955,13 +955,14 @@ __device__ __forceinline__ void split_tile(int bid, const PPSplit &plan, int &v,
 // second waits for the flag (a bounded poll: on time-out it writes NaN
 // rather than hang) and stores alpha (acc + partial) + beta C.  Flag
 // accesses are device-scope for pairs on one XCD, system scope through
-// uncached memory otherwise.
+// uncached memory otherwise.  `ready` is one LDS word the workgroup no
+// longer uses (it passes the poll's outcome to all waves).
 template <int MI, bool EPI>
 __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], float *region,
                                                  __amdgpu_buffer_rsrc_t rc, int row0, int col0,
                                                  int cols_left, int N, float alpha, float beta,
                                                  int split, int v, const PPSplit &split_plan,
-                                                 const float *bias, int act) {
+                                                 const float *bias, int act, int *ready) {
     constexpr int BN = kPPTile;
     const int tid = threadIdx.x;
     if (split < 0) {
@@ -990,22 +991,21 @@ __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], flo
         }
         return;
     }
-    __shared__ int s_ready;
     if (tid == 0) {
-        int ready = 0;
+        int ok = 0;
         for (int poll = 0; poll < (1 << 22); ++poll) {
             const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                 : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             if (f == split_plan.epoch) {
-                ready = 1;
+                ok = 1;
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
         }
-        s_ready = ready;
+        *ready = ok;
     }
     __syncthreads();
-    const float a = s_ready ? alpha : __builtin_nanf("");
+    const float a = *ready ? alpha : __builtin_nanf("");
     if (local)
         store_c_tile_lds128<MI, kAddPartial, kDeviceScope, EPI>(
             acc, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
@@ -1266,8 +1266,9 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
     const int row0 = wm * WM, col0 = wn * WN;
     const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
+    __shared__ int s_ready;
     store_split_tile<MI, EPI>(acc, region, rc, row0, col0, N - n0, N, alpha, beta, split, v,
-                              split_plan, bias, epi.act);
+                              split_plan, bias, epi.act, &s_ready);
 }
 
 
@@ -1414,7 +1415,10 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
             FMT, FMT, 0, 127, 0, 127);
     };
     constexpr int kEarly = 8, kTail = 8;
-    constexpr int kWaitSteady = (2 * COPIES & 15) | (7 << 4) | ((2 * COPIES >> 4) << 14);
+    // at a step's end the copies of the S - 2 later steps may be in flight
+    constexpr int kInFlight = (S - 2) * COPIES;
+    static_assert(kInFlight < 64, "vmcnt holds six bits");
+    constexpr int kWaitSteady = (kInFlight & 15) | (7 << 4) | ((kInFlight >> 4) << 14);
     constexpr int kWaitDrain = (7 << 4);
 
     for (int t = 0; t < S - 1; ++t)
@@ -1487,8 +1491,10 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
                   (static_cast<long long>(M - m0) * N - n0) * 4);
     static_assert(S * STAGE >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
+    // the poll's flag word: B's stages are free once the loop has ended
     store_split_tile<MI, false>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta, split,
-                                v, split_plan, nullptr, kActNone);
+                                v, split_plan, nullptr, kActNone,
+                                reinterpret_cast<int *>(&lds_b[0][0]));
 }
 
 // Calls f(ktail, epi) with the two flags as std::integral_constant values, so
