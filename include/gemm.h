@@ -166,8 +166,11 @@ GEMM_API int gemm_naive_bf16(int M, int N, int K, float alpha, float beta,
  * Products are exact in fp32 and accumulate in fp32; C is float32 in and
  * out.  K % 16 == 0 with 16-byte aligned A and B runs the matrix-core
  * kernel (256 x 256 tiles, v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
- * scales), anything else a one-thread-per-output kernel.  An unknown format
- * and the gemm_bf16 argument errors return GEMM_ERR_INVALID_ARG.
+ * scales), anything else a one-thread-per-output kernel.  As in gemm_bf16, a
+ * last round of tiles that is at most half full is split over K through the
+ * library's per-device workspace (allocated on first use: GEMM_ERR_ALLOC if
+ * that fails; not split while the stream is being captured).  An unknown
+ * format and the gemm_bf16 argument errors return GEMM_ERR_INVALID_ARG.
  */
 enum gemm_fp8_format { GEMM_FP8_E4M3 = 0, GEMM_FP8_E5M2 = 1 };
 GEMM_API int gemm_fp8(int M, int N, int K, float alpha, float beta, const uint8_t *A,
