@@ -83,3 +83,34 @@ def test_pp_split_shape_unsplit_under_capture(torch, tile, monkeypatch):
     s = torch.cuda.Stream()
     name = capture_and_check(torch, case, s, warm=True, want_prefix=tile)
     assert name == tile, name
+
+
+def test_fp8_split_shape_unsplit_under_capture(torch):
+    """The 8-bit float GEMM: a shape split over K when called directly runs
+    whole tiles when captured; every replay (with a direct, split call of the
+    same shape between replays) equals the oracle exactly on integers."""
+    from roofline_driven_optimisation_amd.inputs import f32_to_fp8_bits
+    M, N, K = 1024, 512, 1024
+    rng = np.random.default_rng(83)
+    a = f32_to_fp8_bits(rng.integers(-4, 5, size=(M, K)).astype(np.float32), 0)
+    b = f32_to_fp8_bits(rng.integers(-4, 5, size=(N, K)).astype(np.float32), 0)
+    c0 = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
+    ref, _ = oracle.gemm_fp8(a, b, c0, 1.0, 0.5, 1.0, 1.0, 0)
+    A, B = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    C0 = torch.from_numpy(c0).cuda()
+    C, D = C0.clone(), C0.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.gemm_fp8(A, B, C, 1.0, 0.5)
+    assert binding.last_kernel() == "fp8_q4_256x256x64", binding.last_kernel()
+    for r in range(4):
+        C.copy_(C0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), r
+        D.copy_(C0)
+        binding.gemm_fp8(A, B, D, 1.0, 0.5)
+        assert "splitk" in binding.last_kernel(), binding.last_kernel()
+        torch.cuda.synchronize()
+        assert np.array_equal(D.cpu().numpy().astype(np.float64), ref), r
