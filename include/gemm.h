@@ -29,19 +29,34 @@
  * Workspace.  Two bf16 paths split K across workgroups and exchange partial
  * sums through a scratch area: the decode-shaped (skinny-M) kernel, and the
  * large-M kernel when its last round of 256 x 256 tiles would be at most half
- * full.  The library allocates the area lazily on the first such call for a
- * given (device, stream) pair and reuses it afterwards; it is never freed
- * before process exit.  It is 64 MiB + 128 KiB of uncached device memory
- * (hipExtMallocWithFlags), plus 96 MiB + 64 KiB of ordinary device memory
- * (hipMalloc) through which workgroups that share an XCD exchange partial
- * sums.  Before its first use of the latter on a device, the library runs a
- * small probe grid on the caller's stream and waits for it, to check that the
- * device deals workgroups to its eight XCDs in round-robin order (ids equal
- * modulo 8 share an XCD); where it does not, both paths exchange through the
- * uncached area alone.  Concurrent calls on
+ * full (gemm_fp8 splits such a round too, and reduce_sum_f32 uses the area
+ * for its partial sums).  The library allocates the area lazily on the first
+ * such call for a given (device, stream) pair and reuses it afterwards; it is
+ * never freed before process exit.  It is 64 MiB + 128 KiB of uncached
+ * device memory (hipExtMallocWithFlags), plus 96 MiB + 64 KiB of ordinary
+ * device memory (hipMalloc) through which workgroups that share an XCD
+ * exchange partial sums.  Before its first use of the latter on a device,
+ * the library runs a small probe grid on the caller's stream and waits for
+ * it, to check that the device deals workgroups to its eight XCDs in
+ * round-robin order (ids equal modulo 8 share an XCD); where it does not,
+ * both paths exchange through the uncached area alone.  At most sixteen
+ * streams per device get an area (2.5 GiB at most): calls on further streams run
+ * the same kernels without splitting K (slower on the shapes above, same
+ * results within the tolerances; the vector sums return GEMM_ERR_ALLOC for
+ * vectors long enough to need the area).  Concurrent calls on
  * different streams get different workspaces; concurrent calls from several
- * host threads on one stream must be serialised by the caller, as the stream
- * would serialise them anyway.  The fp32 path never uses a workspace.
+ * host threads on one stream must be serialised by the caller, as the
+ * stream would serialise them anyway.  The fp32 path never uses a
+ * workspace.
+ *
+ * Split pairs.  When a last round of 256 x 256 tiles is split, the two
+ * workgroups of a tile exchange one partial tile: the one that starts first
+ * takes the first part of K, posts its partial and publishes it with a
+ * release store; the other takes the rest and waits for it with an acquire
+ * (a bounded wait on a workgroup that is already running and never waits
+ * itself).  If the wait ever gave up, the tile's C values are NaN and the
+ * call has already returned GEMM_OK; gemm_split_timeouts() reports how many
+ * waits gave up on a stream.
  *
  * Graph capture.  A call on a stream that is being captured into a HIP graph
  * allocates nothing, runs no probe and launches only kernels whose replays
@@ -55,8 +70,9 @@
  * Errors.  No call aborts or throws across the ABI.  Negative sizes, or a
  * NULL pointer for a matrix with a non-zero number of elements, return
  * GEMM_ERR_INVALID_ARG and launch nothing.  A failed
- * launch returns GEMM_ERR_LAUNCH, a failed workspace allocation
- * GEMM_ERR_ALLOC and a failed device query GEMM_ERR_DEVICE.
+ * launch returns GEMM_ERR_LAUNCH, a failed workspace allocation (or, for
+ * the vector sums, no workspace to be had) GEMM_ERR_ALLOC and a failed
+ * device query GEMM_ERR_DEVICE.
  */
 #ifndef MI355X_GEMM_H
 #define MI355X_GEMM_H
@@ -67,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 5
+#define GEMM_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -217,7 +233,10 @@ GEMM_API int gemm_bf16_strided_batched(int batch, int M, int N, int K, float alp
  * the naive form), which bounds the rounding error by that many units of
  * 2^-24 times sum |x|.  n == 0 writes 0.  Asynchronous like the GEMMs; negative n, a NULL out, a NULL x
  * with n > 0 or a misaligned x return GEMM_ERR_INVALID_ARG and launch
- * nothing.  Uses the stream's workspace (as the GEMMs' split-K does).
+ * nothing.  Vectors longer than a few thousand floats are summed by
+ * several workgroups through the stream's workspace (as the GEMMs' split-K
+ * is); GEMM_ERR_ALLOC when no workspace can be had (graph capture on a
+ * stream that has none, or more streams than the library keeps areas for).
  * reduce_sum_f32 is the optimised form (16-byte loads, one workgroup per
  * contiguous chunk); reduce_sum_f32_naive is the page's first version (one
  * element per thread, a shared-memory tree per 256 elements) with the
@@ -236,6 +255,51 @@ GEMM_API const char *gemm_status_string(int status);
  * until the next call on the same thread.  For tests and benchmarks.
  */
 GEMM_API const char *gemm_last_kernel(void);
+
+/*
+ * Name of the kernel that gemm_bf16 (is_bf16 != 0) or gemm_f32 (is_bf16 ==
+ * 0) would launch for an M x N x K call on the current device, without
+ * launching anything: the dispatch rule applied to the kernel signature and
+ * launch configuration of page "Naive GEMM and Roofline analysis", section
+ * 10.2 (which kernel, which grid, for a given M, N, K).  It assumes 16-byte
+ * aligned A, B and C and a call on the null stream that is not being
+ * captured, and reads the same MGEMM_* environment overrides as the calls.
+ * Before the first call that needed the XCD probe on this device, it
+ * assumes the probe passes.  Returns "none" for M == 0 or N == 0,
+ * "scale_c" for K == 0, "invalid" for negative sizes or a failed device
+ * query.  Static storage, never NULL.
+ */
+GEMM_API const char *gemm_kernel_name(int is_bf16, int M, int N, int K);
+
+/*
+ * Diagnostic: how many split-pair waits gave up (and wrote NaN into their
+ * tile) on `stream` (current device) since the previous call; *count is set
+ * to that number and the count is cleared.  Waits on `stream` first (it
+ * copies the count back), so it must not be called while the stream is
+ * being captured (GEMM_ERR_INVALID_ARG).  A stream without a workspace
+ * reports 0.  NULL count: GEMM_ERR_INVALID_ARG.
+ */
+GEMM_API int gemm_split_timeouts(void *stream, long long *count);
+
+/*
+ * Test hooks.  They change how later calls behave, so that tests can reach
+ * paths that normal inputs never take; every kernel still runs to its end.
+ *   GEMM_TEST_POLL_LIMIT  the number of flag reads a split pair's second
+ *                         workgroup makes before it gives up (value < 0
+ *                         restores the default, about half a second's
+ *                         worth; 0 makes every such wait give up at once);
+ *                         process-wide; `stream` is ignored.
+ *   GEMM_TEST_EPOCH       sets the last split epoch used on `stream`'s
+ *                         workspace (current device) to (uint32_t)value, so
+ *                         that a test can run calls across the point where
+ *                         the 32-bit epoch wraps to zero (the library then
+ *                         clears the flags on the stream and restarts at 1);
+ *                         GEMM_ERR_INVALID_ARG if the stream has no
+ *                         workspace yet.
+ * An unknown hook returns GEMM_ERR_INVALID_ARG.
+ */
+enum gemm_test_hook_id { GEMM_TEST_POLL_LIMIT = 1, GEMM_TEST_EPOCH = 2 };
+GEMM_API int gemm_test_hook(int hook, long long value, void *stream);
 
 /* GEMM_ABI_VERSION of the built library. */
 GEMM_API int gemm_abi_version(void);

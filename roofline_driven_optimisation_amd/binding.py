@@ -72,6 +72,12 @@ def library():
         lib.gemm_last_kernel.restype = ctypes.c_char_p
         lib.gemm_abi_version.argtypes = []
         lib.gemm_abi_version.restype = ctypes.c_int
+        lib.gemm_kernel_name.argtypes = [i, i, i, i]
+        lib.gemm_kernel_name.restype = ctypes.c_char_p
+        lib.gemm_split_timeouts.argtypes = [vp, ctypes.POINTER(ctypes.c_longlong)]
+        lib.gemm_split_timeouts.restype = ctypes.c_int
+        lib.gemm_test_hook.argtypes = [i, ctypes.c_longlong, vp]
+        lib.gemm_test_hook.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -83,6 +89,36 @@ def _status_message(status: int) -> str:
 def last_kernel() -> str:
     """Name of the kernel the last call on this thread launched."""
     return library().gemm_last_kernel().decode()
+
+
+def kernel_name(dtype: str, M: int, N: int, K: int) -> str:
+    """The kernel gemm_bf16 (dtype "bf16") or gemm_f32 ("f32") would launch
+    for an M x N x K call on the current device, without launching it."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return library().gemm_kernel_name(1 if dtype == "bf16" else 0, int(M), int(N),
+                                      int(K)).decode()
+
+
+# enum gemm_test_hook_id
+TEST_POLL_LIMIT, TEST_EPOCH = 1, 2
+
+
+def split_timeouts(stream=None) -> int:
+    """Split-pair waits that gave up on the stream since the last query
+    (waits for the stream; clears the count)."""
+    count = ctypes.c_longlong(0)
+    status = library().gemm_split_timeouts(_stream_handle(stream), ctypes.byref(count))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
+    return int(count.value)
+
+
+def set_test_hook(hook: int, value: int, stream=None) -> None:
+    """Set one of the library's test hooks (see gemm_test_hook in gemm.h)."""
+    status = library().gemm_test_hook(int(hook), int(value), _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
 
 
 def _stream_handle(stream):

@@ -10,19 +10,22 @@
 //     and running MFMAs (ping-pong), so MFMAs do not wait on LDS reads.
 // The tile picker at the end chooses between them by shape.
 //
-// Last-round split (ping-pong kernel).  A 256 x 256 tile count that leaves a
-// last round at most half full (2048 x 4096: 128 tiles; 2048 x 12288: 384 on
-// 256 CUs) wastes up to half of that round.  Its r tiles are then computed
-// by 2 r workgroups, each over half of the K steps: the lower-numbered one
-// of a pair posts its fp32 partial tile and raises a flag (an epoch number
-// chosen by the host per call); the higher-numbered one waits for the flag
-// and writes alpha * (own + partial) + beta * C.  Only the higher-numbered
-// workgroup waits and workgroups are dispatched in increasing id order, so
-// the wait always ends; the sum of two partials does not depend on the order
-// in which they are added.  When r is a multiple of 8 the pair is workgroups
-// b and b + 8, which the hardware places on the same XCD, and the partial
-// goes through that XCD's L2 in ordinary memory; otherwise the pair is 2i
-// and 2i + 1, on different XCDs, and the partial goes through uncached
+// Last-round split (both 256 x 256 kernels and the 8-bit float kernel).  A
+// 256 x 256 tile count that leaves a last round at most half full (2048 x
+// 4096: 128 tiles; 2048 x 12288: 384 on 256 CUs) wastes up to half of that
+// round.  Its r tiles are then computed by 2 r workgroups, each over part of
+// the K steps: the first of a pair to start posts its fp32 partial tile and
+// publishes it (release store of an epoch number the host chose for the
+// call); the second waits for it (acquire) and writes alpha * (own +
+// partial) + beta * C.  Roles are decided when the workgroups start (an
+// atomic swap on the tile's claim word: the first to claim posts), so a
+// workgroup only waits for one that is already running and never waits
+// itself, and the wait ends whatever order the hardware dispatched the
+// workgroups in; the sum of two partials does not depend on the order in
+// which they are added.  When r is a multiple of 8 the pair is
+// workgroups b and b + 8, which the hardware places on the same XCD, and the
+// partial goes through that XCD's L2 in ordinary memory; otherwise the pair
+// is 2i and 2i + 1, on different XCDs, and the partial goes through uncached
 // memory.  The pages do not cover this; it is the split-K idea applied to
 // the wave-quantisation loss they discuss for small grids.
 //
@@ -665,6 +668,111 @@ __device__ __forceinline__ int swz_a32(int r) { return (r >> 2) & 3; }
 // lgkmcnt 11:8 left at their maxima).
 constexpr int wait_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
 
+// ---- the split pair's handshake (see PPSplit) ------------------------------
+// LOCAL pairs share one XCD and exchange through ordinary memory whose
+// coherence point for both is that XCD's L2: device (agent) scope.  Other
+// pairs exchange through uncached memory: system scope.  Each function is
+// called by every thread of the workgroup; `word` is an LDS int used to
+// broadcast thread 0's result, a different one for each function.
+
+// The split index of this workgroup: 0 if it is the first of its pair to
+// claim the tile, 1 if the second.  Called at the kernel's start: thread 0
+// swaps the epoch into the tile's claim word (the swap only decides the
+// roles, so it needs no ordering of its own).  The first to claim is then
+// running and never waits, so the second, which waits for it, waits for a
+// workgroup that will finish.
+template <bool LOCAL>
+__device__ __forceinline__ int pair_arrive(const PPSplit &p, int slot, int *word) {
+    if (threadIdx.x == 0) {
+        const unsigned old =
+            LOCAL ? __hip_atomic_exchange(p.claims + slot, p.epoch, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                  : __hip_atomic_exchange(p.claims + slot, p.epoch, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+        *word = old == p.epoch;
+    }
+    __syncthreads();
+    return *word;
+}
+
+// The first of a pair, after every wave has stored its share of the partial
+// tile: the barrier orders all of them before thread 0's release store of
+// the flag.
+template <bool LOCAL>
+__device__ __forceinline__ void pair_publish(const PPSplit &p, int slot) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (LOCAL)
+            __hip_atomic_store(p.flags + slot, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(p.flags + slot, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+// The second of a pair: wait until the first has published its partial.
+// Thread 0 polls with relaxed loads, at most poll_limit of them, and then
+// takes an acquire fence; the barrier hands the ordering on to the other
+// waves.  Returns false (after counting the time-out) if the flag never
+// came; the first workgroup of the pair is already past its K loop, so that
+// only happens when poll_limit is too small for the partial's store.
+template <bool LOCAL>
+__device__ __forceinline__ bool pair_wait(const PPSplit &p, int slot, int *word) {
+    if (threadIdx.x == 0) {
+        int ready = 0;
+        for (int poll = 0; poll < p.poll_limit; ++poll) {
+            const unsigned f =
+                LOCAL ? __hip_atomic_load(p.flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : __hip_atomic_load(p.flags + slot, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+            if (f == p.epoch) {
+                ready = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (ready) {
+            if (LOCAL)
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            else
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+        } else if (p.timeouts != nullptr) {
+            __hip_atomic_fetch_add(p.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        *word = ready;
+    }
+    __syncthreads();
+    return *word != 0;
+}
+
+// Tile and K half of workgroup `bid` under a split plan: workgroups below
+// split_from own a whole tile (XCD-aware order, split = -1); the rest come
+// in pairs that share a tile.  With xcd_pairs, workgroups b and b + 8 pair
+// up (one XCD under round-robin dealing), else 2i and 2i + 1.  Of a pair,
+// the first to claim the tile (pair_arrive) is split 0, which takes the K
+// steps before split_step and posts its partial; the other is split 1,
+// which takes the rest, waits for the partial and writes C.  So the
+// workgroup that started first gets the shorter half, and the one that
+// waits only ever waits for a running workgroup.  Every thread of the
+// workgroup calls this (it has a barrier when the tile is split).
+__device__ __forceinline__ void split_tile(int bid, const PPSplit &plan, int &v, int &split,
+                                           int *word) {
+    split = -1;
+    if (bid < plan.split_from) {
+        v = xcd_remap(bid, plan.split_from);
+        return;
+    }
+    const int q = bid - plan.split_from;
+    if (plan.xcd_pairs) {
+        const int p = (q >> 4) * 8 + (q & 7);
+        v = plan.split_from + xcd_remap(p, plan.grid_tiles - plan.split_from);
+        split = pair_arrive<true>(plan, v - plan.split_from, word);
+    } else {
+        v = plan.split_from + (q >> 1);
+        split = pair_arrive<false>(plan, v - plan.split_from, word);
+    }
+}
+
 template <int BM, int BN, int S, bool KTAIL, bool EPI>
 __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, float alpha,
                                                          float beta,
@@ -680,22 +788,9 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     // whole tile (XCD-aware order); the rest come in pairs that share one of
     // the remaining tiles: the first takes the K steps below split_step and
     // posts its partial sums, the second takes the rest and adds them.
-    const int bid = blockIdx.x;
-    int v, split = -1;
-    if (bid < split_plan.split_from) {
-        v = xcd_remap(bid, split_plan.split_from);
-    } else if (split_plan.xcd_pairs) {
-        // workgroups b and b + 8 share a tile, so both run on one XCD; the
-        // pairs of an XCD take consecutive tiles
-        const int q = bid - split_plan.split_from;
-        const int p = (q >> 4) * 8 + (q & 7);
-        v = split_plan.split_from + xcd_remap(p, (split_plan.grid_tiles - split_plan.split_from));
-        split = (q >> 3) & 1;
-    } else {
-        const int q = bid - split_plan.split_from;
-        v = split_plan.split_from + (q >> 1);
-        split = q & 1;
-    }
+    int v, split;
+    __shared__ int s_role, s_ready;
+    split_tile(blockIdx.x, split_plan, v, split, &s_role);
     int tm, tn;
     grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -880,46 +975,21 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
     const int slot = v - split_plan.split_from;
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BM * BN, BM * BN * 4);
-    int *flag = split_plan.flags + slot;
-    // Uncached workspace (pairs on different XCDs): system-scope flag
-    // accesses reach memory.  XCD-local pairs use ordinary memory whose
-    // coherence point for both is their L2: the flag is stored with device
-    // scope and polled with device-scope loads, which skip the CU's L1.
     const bool local = split_plan.xcd_pairs != 0;
     if (split == 0) {
         store_c_tile_lds<T::MI, T::NI, kPostPartial>(acc, region, rc, row0, col0, N - n0, N,
                                                      alpha, beta, rw, BN);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
-        __syncthreads();
-        if (tid == 0) {
-            if (local)
-                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            else
-                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
-        }
+        if (local)
+            pair_publish<true>(split_plan, slot);
+        else
+            pair_publish<false>(split_plan, slot);
         return;
     }
-    // The second of the pair waits for the first's flag.  The first has a
-    // lower workgroup id, is dispatched no later and never waits, so the
-    // wait ends; a bounded poll turns anything else into NaN output.
-    __shared__ int s_ready;
-    if (tid == 0) {
-        int ready = 0;
-        for (int poll = 0; poll < (1 << 22); ++poll) {
-            const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            if (f == split_plan.epoch) {
-                ready = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        s_ready = ready;
-    }
-    __syncthreads();
-    const float a = s_ready ? alpha : __builtin_nanf("");
+    const bool ok = local ? pair_wait<true>(split_plan, slot, &s_ready)
+                          : pair_wait<false>(split_plan, slot, &s_ready);
+    const float a = ok ? alpha : __builtin_nanf("");
+    // partial loads: device scope (skip the CU's L1) for pairs on one XCD,
+    // system scope through uncached memory otherwise
     if (local)
         store_c_tile_lds<T::MI, T::NI, kAddPartial, kDeviceScope, EPI>(
             acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
@@ -928,43 +998,20 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
             acc, region, rc, row0, col0, N - n0, N, a, beta, rw, BN, bias, epi.act);
 }
 
-// Tile and K half of workgroup `bid` under a split plan: workgroups below
-// split_from own a whole tile (XCD-aware order, split = -1); the rest come
-// in pairs that share a tile, split 0 taking the K steps before split_step
-// and split 1 the others.  With xcd_pairs, workgroups b and b + 8 pair up
-// (one XCD under round-robin dealing), else 2i and 2i + 1.
-__device__ __forceinline__ void split_tile(int bid, const PPSplit &plan, int &v, int &split) {
-    split = -1;
-    if (bid < plan.split_from) {
-        v = xcd_remap(bid, plan.split_from);
-    } else if (plan.xcd_pairs) {
-        const int q = bid - plan.split_from;
-        const int p = (q >> 4) * 8 + (q & 7);
-        v = plan.split_from + xcd_remap(p, plan.grid_tiles - plan.split_from);
-        split = (q >> 3) & 1;
-    } else {
-        const int q = bid - plan.split_from;
-        v = plan.split_from + (q >> 1);
-        split = q & 1;
-    }
-}
 
 // The epilogue of a 256 x 256 four-wave tile under a split plan: a whole
-// tile stores alpha acc + beta C; the first of a split pair posts its
-// partial to the pair's workspace slot and raises the slot's flag; the
-// second waits for the flag (a bounded poll: on time-out it writes NaN
-// rather than hang) and stores alpha (acc + partial) + beta C.  Flag
-// accesses are device-scope for pairs on one XCD, system scope through
-// uncached memory otherwise.  `ready` is one LDS word the workgroup no
-// longer uses (it passes the poll's outcome to all waves).
+// tile stores alpha acc + beta C; of a split pair, split 0 posts its partial
+// to the pair's workspace slot and publishes it, split 1 waits for it
+// (pair_wait: on time-out it writes NaN rather than hang) and stores alpha
+// (acc + partial) + beta C.  `word` is an LDS int the workgroup no longer
+// uses (it broadcasts the wait's outcome).
 template <int MI, bool EPI>
 __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], float *region,
                                                  __amdgpu_buffer_rsrc_t rc, int row0, int col0,
                                                  int cols_left, int N, float alpha, float beta,
                                                  int split, int v, const PPSplit &split_plan,
-                                                 const float *bias, int act, int *ready) {
+                                                 const float *bias, int act, int *word) {
     constexpr int BN = kPPTile;
-    const int tid = threadIdx.x;
     if (split < 0) {
         store_c_tile_lds128<MI, kStoreC, kSystemScope, EPI>(acc, region, rc, row0, col0,
                                                             cols_left, N, alpha, beta, rc, 0,
@@ -974,38 +1021,19 @@ __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], flo
     const int slot = v - split_plan.split_from;
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BN * BN, BN * BN * 4);
-    int *flag = split_plan.flags + slot;
     const bool local = split_plan.xcd_pairs != 0;
     if (split == 0) {
         store_c_tile_lds128<MI, kPostPartial>(acc, region, rc, row0, col0, cols_left, N, alpha,
                                               beta, rw, BN);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
-        __syncthreads();
-        if (tid == 0) {
-            if (local)
-                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            else
-                __hip_atomic_store(flag, split_plan.epoch, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
-        }
+        if (local)
+            pair_publish<true>(split_plan, slot);
+        else
+            pair_publish<false>(split_plan, slot);
         return;
     }
-    if (tid == 0) {
-        int ok = 0;
-        for (int poll = 0; poll < (1 << 22); ++poll) {
-            const int f = local ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            if (f == split_plan.epoch) {
-                ok = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        *ready = ok;
-    }
-    __syncthreads();
-    const float a = *ready ? alpha : __builtin_nanf("");
+    const bool ok = local ? pair_wait<true>(split_plan, slot, word)
+                          : pair_wait<false>(split_plan, slot, word);
+    const float a = ok ? alpha : __builtin_nanf("");
     if (local)
         store_c_tile_lds128<MI, kAddPartial, kDeviceScope, EPI>(
             acc, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
@@ -1066,7 +1094,8 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     // split_from own a whole tile (XCD-aware order) and the rest come in
     // pairs that share a tile, one per half of the K steps.
     int v, split;
-    split_tile(blockIdx.x, split_plan, v, split);
+    __shared__ int s_words[2];
+    split_tile(blockIdx.x, split_plan, v, split, &s_words[0]);
     // A batched launch (never split) numbers the tiles of all items in
     // turn: the XCD-aware order keeps one item's tiles on one XCD.
     const int per_item = tiles_m * tiles_n;
@@ -1266,9 +1295,8 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
     const int row0 = wm * WM, col0 = wn * WN;
     const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
-    __shared__ int s_ready;
     store_split_tile<MI, EPI>(acc, region, rc, row0, col0, N - n0, N, alpha, beta, split, v,
-                              split_plan, bias, epi.act, &s_ready);
+                              split_plan, bias, epi.act, &s_words[1]);
 }
 
 
@@ -1327,7 +1355,8 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
 
     // tile and K range under the split plan (as the bf16 four-wave kernel)
     int v, split;
-    split_tile(blockIdx.x, split_plan, v, split);
+    __shared__ int s_words[2];
+    split_tile(blockIdx.x, split_plan, v, split, &s_words[0]);
     int tm, tn;
     grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -1491,10 +1520,8 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
                   (static_cast<long long>(M - m0) * N - n0) * 4);
     static_assert(S * STAGE >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
     float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
-    // the poll's flag word: B's stages are free once the loop has ended
     store_split_tile<MI, false>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta, split,
-                                v, split_plan, nullptr, kActNone,
-                                reinterpret_cast<int *>(&lds_b[0][0]));
+                                v, split_plan, nullptr, kActNone, &s_words[1]);
 }
 
 // Calls f(ktail, epi) with the two flags as std::integral_constant values, so
@@ -1513,12 +1540,14 @@ void with_flags(bool ktail, bool epi, F &&f) {
 // Checks a split plan against the tile count and K; fills `plan` (whole
 // tiles only when split is null).
 bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan, int bk = kPPBK) {
-    plan = {static_cast<int>(tiles), 0, nullptr, nullptr, 0, 0, static_cast<int>(tiles)};
+    plan = PPSplit{static_cast<int>(tiles), 0, nullptr, nullptr, nullptr, 0u, 0,
+                   static_cast<int>(tiles), 0, nullptr};
     if (split == nullptr) return true;
     const int steps = (K + bk - 1) / bk;
     if (split->split_from < 0 || split->split_from > tiles || split->split_step < 1 ||
-        split->split_step >= steps ||
-        (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr)) ||
+        split->split_step >= steps || split->poll_limit < 0 ||
+        (split->split_from < tiles && (split->partials == nullptr || split->flags == nullptr ||
+                                       split->claims == nullptr)) ||
         (split->xcd_pairs && (tiles - split->split_from) % 8 != 0))
         return false;
     plan = *split;

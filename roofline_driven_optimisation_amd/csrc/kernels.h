@@ -66,21 +66,37 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split);
 // workgroups, one per half of the K steps: the first posts its partial sums,
 // the second adds them and writes C, so the last round takes about half as
 // long on twice as many CUs.
+//
+// The pair's handshake.  When a workgroup of a pair has finished its K
+// steps, one thread swaps the epoch into the tile's claim word: the first to
+// arrive (old value != epoch) posts its partial tile and then publishes the
+// epoch in the tile's flag with a release store; the second waits for the
+// flag with an acquire, adds the partial to its own sums and writes C.  The
+// second thus only ever waits for a workgroup that is already past its K
+// loop, whatever order the workgroups were dispatched in.  The wait is
+// bounded by poll_limit flag reads; a wait that gives up writes NaN into its
+// tile and adds one to *timeouts, which the host can read back.
 constexpr int kPPTile = 256;  // the square tile of both 256 x 256 kernels
+constexpr int kPollLimitDefault = 1 << 22;  // flag reads, about 0.5 s
 struct PPSplit {
     int split_from;   // tiles at or past this position in the order are split
     int split_step;   // first K step (of 32) of the second half
-    float *partials;  // one kPPTile^2 fp32 tile per split tile, uncached memory
-    int *flags;       // one int per split tile, uncached, never equal to epoch on entry
-    int epoch;        // a value the flags have not held before this launch
-    // 0: workgroups 2i and 2i + 1 share a tile (different XCDs); partials and
-    // flags must be uncached.  1: workgroups b and b + 8 share a tile, which
-    // puts both on one XCD on a device that deals workgroups to its eight
-    // XCDs in round-robin order (probe_xcd_mapping checks this);
-    // partials and flags are ordinary device memory that no other XCD uses
-    // during the launch, and the number of split tiles is a multiple of 8.
+    float *partials;  // one kPPTile^2 fp32 tile per split tile
+    unsigned *flags;  // one word per split tile, never equal to epoch on entry
+    unsigned *claims; // one word per split tile, never equal to epoch on entry
+    unsigned epoch;   // a value flags and claims have not held before this launch
+    // 0: workgroups 2i and 2i + 1 share a tile (different XCDs); partials,
+    // flags and claims must be uncached memory and their accesses are
+    // system-scope.  1: workgroups b and b + 8 share a tile, which puts both
+    // on one XCD on a device that deals workgroups to its eight XCDs in
+    // round-robin order (probe_xcd_mapping checks this); partials, flags and
+    // claims are ordinary device memory that no other XCD uses during the
+    // launch, their accesses are device-scope, and the number of split tiles
+    // is a multiple of 8.
     int xcd_pairs;
-    int grid_tiles;   // set by the launcher: the tile count
+    int grid_tiles;      // set by the launcher: the tile count
+    int poll_limit;      // flag reads before a waiting workgroup gives up
+    unsigned *timeouts;  // uncached word counting waits that gave up (may be null)
 };
 int bf16_pp_config();                                          // the ping-pong tile index
 bool bf16_config_splits(int cfg);  // the 256 x 256 kernels, which can split a last round

@@ -39,8 +39,13 @@ def run(case, kernel="auto", stream=None, c_fill=np.nan):
         case.name, case.M, case.N, case.K, case.dtype, case.alpha, case.beta, kernel))
     fn = {"auto": binding.gemm, "naive": (binding.gemm_naive_bf16 if case.bf16
                                           else binding.gemm_naive_f32)}[kernel]
+    # the pure dispatch query names the kernel before the call launches it
+    # (it assumes the null stream, which torch's default stream is)
+    predicted = binding.kernel_name(case.dtype, case.M, case.N, case.K)
     fn(A, B, C, case.alpha, case.beta, stream=stream)
     name = binding.last_kernel()
+    if kernel == "auto" and stream is None:
+        assert predicted == name, "gemm_kernel_name %s, launched %s" % (predicted, name)
     torch.cuda.synchronize()
     return C.cpu().numpy(), name
 

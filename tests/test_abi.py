@@ -33,7 +33,8 @@ def test_header_declares_expected_api():
     names = declared_functions()
     for n in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16",
               "gemm_f32_bias_act", "gemm_bf16_bias_act", "reduce_sum_f32", "reduce_sum_f32_naive",
-              "gemm_bf16_strided_batched", "gemm_fp8",
+              "gemm_bf16_strided_batched", "gemm_fp8", "gemm_kernel_name",
+              "gemm_split_timeouts", "gemm_test_hook",
               "gemm_status_string", "gemm_last_kernel", "gemm_abi_version"):
         assert n in names
 
@@ -85,3 +86,24 @@ def test_binding_rejects_bad_tensors():
     A = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         binding.gemm_f32(A, A, A)  # CPU tensors are refused before any call
+
+
+def test_kernel_name_without_gpu(lib):
+    """The dispatch query answers the cases that need no device: the fp32
+    kernel choice depends only on K and N modulo 4, and empty or negative
+    shapes are answered before any device query."""
+    assert lib.gemm_kernel_name(0, 4096, 4096, 4096) == b"f32_mfma_128x128x32_vec4"
+    assert lib.gemm_kernel_name(0, 4092, 4092, 4092) == b"f32_mfma_128x128x32_vec4"
+    assert lib.gemm_kernel_name(0, 5, 7, 3) == b"f32_mfma_128x128x32_scalar"
+    assert lib.gemm_kernel_name(0, 5, 6, 8) == b"f32_mfma_128x128x32_scalar"
+    for is_bf16 in (0, 1):
+        assert lib.gemm_kernel_name(is_bf16, 0, 8, 8) == b"none"
+        assert lib.gemm_kernel_name(is_bf16, 8, 0, 8) == b"none"
+        assert lib.gemm_kernel_name(is_bf16, 8, 8, 0) == b"scale_c"
+        assert lib.gemm_kernel_name(is_bf16, -1, 8, 8) == b"invalid"
+        assert lib.gemm_kernel_name(is_bf16, 8, 8, -1) == b"invalid"
+
+
+def test_diagnostics_argument_errors(lib):
+    assert lib.gemm_split_timeouts(None, None) == 1
+    assert lib.gemm_test_hook(99, 0, None) == 1
