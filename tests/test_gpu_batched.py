@@ -3,8 +3,8 @@ stored token-major, and O = P V) through the C ABI, against the oracle item
 by item: every path (the four-wave 256 x 256 kernel with B as K x N or
 stored transposed, the 128 x 128 kernel for N <= 128, the
 one-thread-per-output fallback), exact on integer inputs, within the bf16 tolerance on random
-ones, and at the attention shapes of a 2048-token, 32-head, d = 128 layer on
-sampled entries."""
+ones, and at the attention shapes of a 2048-token, 32-head, d = 128 layer
+over every head's whole output."""
 import ctypes
 
 import numpy as np
@@ -82,10 +82,10 @@ def test_batched_random(case):
 
 
 @pytest.mark.parametrize("trans_b", [True, False], ids=["qk", "pv"])
-def test_attention_shapes_sampled(trans_b):
+def test_attention_shapes_full(trans_b):
     """32 heads, 2048 tokens, d = 128: S = Q K^T (M = N = 2048, K = 128, K
-    stored token-major) and O = P V (M = 2048, N = 128, K = 2048)."""
-    import torch
+    stored token-major) and O = P V (M = 2048, N = 128, K = 2048), every
+    head's whole output against the oracle."""
     H, T, d = 32, 2048, 128
     M, N, K = (T, T, d) if trans_b else (T, d, T)
     rng = np.random.default_rng(3)
@@ -93,14 +93,13 @@ def test_attention_shapes_sampled(trans_b):
     B = f32_to_bf16_bits(draw((H, N, K) if trans_b else (H, K, N), "n:0.1", rng))
     got, name = run(A, B, None, 1.0, 0.0, trans_b, N)
     assert name.startswith("bf16_"), name
-    for h in (0, 13, 31):
-        rows = rng.integers(0, M, 300)
-        cols = rng.integers(0, N, 300)
+    worst = 0.0
+    for h in range(H):
         Bh = np.ascontiguousarray(B[h].T) if trans_b else B[h]
-        ref, den = oracle.gemm_entries(A[h], Bh, rows, cols, bf16=True)
-        err = oracle.parity_error(got[h][rows, cols], ref, den)
-        log("  attention %s head %d err=%.3e" % ("qk" if trans_b else "pv", h, err))
-        assert err <= TOL["bf16"]
+        ref, den = oracle.gemm(A[h], Bh, bf16=True)
+        worst = max(worst, oracle.parity_error(got[h], ref, den))
+    log("  attention %s, all %d heads, err=%.3e" % ("qk" if trans_b else "pv", H, worst))
+    assert worst <= TOL["bf16"]
 
 
 def test_shared_operand_stride_zero():

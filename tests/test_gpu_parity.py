@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (TOL, check_full, check_row_checksums, check_sampled, log, run,
+from gpu_helpers import (TOL, check_full, check_row_checksums, log, run,
                          to_device, operands_f64)
 from roofline_driven_optimisation_amd import binding
 from roofline_driven_optimisation_amd.inputs import (WORKLOADS, f32_to_bf16_bits, make_case,
@@ -99,23 +99,22 @@ FULL = [w.name for w in WORKLOADS if w.name != "f32_256"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_workload_sampled(name):
+def test_workload_full(name):
     """Every full-size workload, in the launch configuration the benchmark
-    times, checked on sampled entries (edges and tile borders included) and
-    on per-row checksums of the whole output."""
+    times, compared element by element with the oracle over the whole
+    output (the oracle computes a 4096^3 product in a few seconds on the
+    host's cores), plus the per-row checksum property."""
     w = workload(name)
     case = w.case()
     C, kname = run(case)
     log("  kernel %s" % kname)
-    if w.M <= 16:
-        check_full(case, C)  # decode shapes are small enough for the full oracle
-    else:
-        check_sampled(case, C, count=4096)
+    check_full(case, C)
     check_row_checksums(case, C)
 
 
-@pytest.mark.parametrize("name", ["f32_4092", "f32_4096", "bf16_4096", "prefill_down",
-                                  "prefill_gate_up", "decode_down_m16", "decode_lm_head"])
+@pytest.mark.parametrize("name", ["f32_4092", "f32_4096", "bf16_4096", "prefill_qkv",
+                                  "prefill_o", "prefill_down", "prefill_gate_up",
+                                  "decode_down_m16", "decode_lm_head"])
 def test_workload_integer_exact(name):
     """Full-size shapes with integer entries in [-2, 2]: the exact product is
     known in fp64 for every element, so the whole output must match it."""
@@ -434,7 +433,37 @@ def test_side_stream(gpu):
         case = make_case(w.M, w.N, min(w.K, 1024), w.dtype, 1.0, 0.0, w.dist_a, w.dist_b, seed=25)
         with torch.cuda.stream(s):
             C, _ = run(case, stream=s)
-        check_full(case, C) if case.M <= 16 else check_sampled(case, C)
+        check_full(case, C)
+
+
+# One shape per dispatch path (bf16 unless noted): the pure query
+# gemm_kernel_name must name the kernel the call then launches (run()
+# asserts it), and the result must be exact on integer inputs.
+QUERY_SHAPES = [
+    ("f32", 256, 256, 256),      # fp32, 16-byte rows
+    ("f32", 5, 7, 3),            # fp32, element-wise loads
+    ("bf16", 16, 4096, 4096),    # skinny, XCD-local split-K
+    ("bf16", 16, 896, 4096),     # skinny, split-K through uncached memory (7 column blocks)
+    ("bf16", 4, 1024, 256),      # skinny, one split
+    ("bf16", 256, 256, 512),     # 256 x 256, one tile split across XCDs
+    ("bf16", 512, 1024, 512),    # 256 x 256, eight split tiles paired on one XCD
+    ("bf16", 512, 512, 128),     # tiled, too few K steps to split
+    ("bf16", 4096, 4096, 64),    # tiled, one full round
+    ("bf16", 64, 100, 64),       # N % 8 != 0: one thread per output
+    ("bf16", 8, 100, 64),        # decode-shaped but N % 8 != 0
+    ("bf16", 8, 64, 0),          # K = 0
+]
+
+
+@pytest.mark.parametrize("q", QUERY_SHAPES, ids=lambda q: "%s_%dx%dx%d" % q)
+def test_kernel_name_query(q):
+    dtype, M, N, K = q
+    case = make_case(M, N, K, dtype, 1.5, 0.5, "i:4", "i:4", "i:4", seed=26)
+    want = binding.kernel_name(dtype, M, N, K)
+    C, name = run(case)
+    assert name == want, (want, name)
+    Cref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=case.bf16)
+    assert np.array_equal(C.astype(np.float64), Cref)
 
 
 def test_dispatch_names():
