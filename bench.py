@@ -18,8 +18,13 @@ by device synchronisations.  The same line carries:
 * ``ladder``: the one-thread-per-output kernel against the tiled one on
   fp32 4092^3, the first and last rungs of the optimisation ladder;
 * ``page_context``: the figures the pages quote for other machines;
-* ``cpu_baseline``: the CPU oracle, as it stands, timed on a bounded sample
-  of the headline workload (rank 0, N = 1 only).
+* ``cpu_baseline``: the CPU oracle, as it stands, timed (rank 0, N = 1 only)
+  on the whole headline GEMM and on sampled rows of every other workload,
+  with a per-configuration list and configuration 1 also single-threaded;
+* ``parity`` (for the headline, and in each ``also`` entry): after each
+  workload's timed loop, one more launch keeps sampled rows of its output,
+  which the oracle leg above compares with its own rows (max |C - C_ref| /
+  den against the workload's tolerance).
 
 ``--sustain SECONDS`` instead launches a workload back to back and samples
 the GFX clock and board power with amd-smi (the GEMM runs at the power limit).
@@ -137,6 +142,55 @@ class Prepared:
         self.launch(0)
         return binding.last_kernel()
 
+    # -- parity of a sampled block, outside the timed region --------------
+    def rows_for(self, budget_flop):
+        return sample_rows(self.w.M, self.w.N, self.w.K, budget_flop)
+
+    def verify_launch(self, rows):
+        """One more launch on operand set 0 (C restored first when beta !=
+        0); returns the GPU output's `rows`."""
+        import torch
+        A, B, C = self.bufs[0]
+        if self.C0 is not None:
+            C.copy_(self.C0)
+        self.launch(0)
+        torch.cuda.synchronize()
+        if self.epi is not None:
+            self.bias_host = self.epi[0].cpu().numpy()
+        return C[torch.from_numpy(rows).cuda()].cpu().numpy()
+
+    def oracle_rows(self, rows):
+        """(reference, denominator, FLOPs) of the oracle on `rows`."""
+        import oracle
+        c = self.case
+        bias = act = None
+        if self.epi is not None:
+            bias, act = self.bias_host, self.epi[1]
+        ref, den = oracle.gemm(c.A[rows], c.B, c.C[rows] if c.C is not None else None,
+                               c.alpha, c.beta, bf16=c.bf16, bias=bias, act=act or 0)
+        return ref, den, 2.0 * len(rows) * c.N * c.K
+
+    def tolerance(self):
+        tol = 4e-3 if self.case.bf16 else 1e-5
+        if self.epi is not None:  # |act'| bounds how far an error moves the output
+            tol *= {0: 1.0, 1: 1.0, 2: 1.13, 3: 1.10}[self.epi[1]]
+        return tol
+
+
+def sample_rows(M, N, K, budget_flop):
+    """Output rows checked against the oracle: all of them when the budget
+    allows (and always at M <= 16), else equal numbers of leading and
+    trailing rows (the first and the last, possibly ragged, tile rows)."""
+    per_row = 2.0 * N * K
+    if M <= 16 or budget_flop == float("inf"):
+        count = M
+    else:
+        count = int(min(M, max(2, budget_flop // per_row)))
+    if count >= M:
+        return np.arange(M, dtype=np.int64)
+    half = max(1, count // 2)
+    return np.concatenate([np.arange(half), np.arange(M - half, M)]).astype(np.int64)
+
 
 class PreparedSum:
     """The vector-sum workload "sum_<n>": n float32 values ~ U[-1, 1] (seed
@@ -157,6 +211,25 @@ class PreparedSum:
     def launch(self, i: int, naive: bool = False):
         from roofline_driven_optimisation_amd import binding
         binding.reduce_sum_f32(self.bufs[i % self.sets], self.out, naive=naive)
+
+    def rows_for(self, budget_flop):
+        return None  # the whole vector
+
+    def verify_launch(self, rows):
+        import torch
+        self.x_host = self.bufs[0].cpu().numpy()
+        self.launch(0)
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()[:1]
+
+    def oracle_rows(self, rows):
+        import oracle
+        s, a = oracle.sum_f32(self.x_host)
+        return np.array([s]), np.array([a + 1e-30]), float(self.n)
+
+    def tolerance(self):
+        # at most n / 2^21 + 32 fp32 additions per element (80 at 10^8)
+        return (self.n / 2.0 ** 21 + 32) * 2.0 ** -24
 
     def kernel_name(self) -> str:
         from roofline_driven_optimisation_amd import binding
@@ -199,6 +272,27 @@ class PreparedBatched:
         A, B, C = self.bufs[i % self.sets]
         binding.gemm_bf16_batched(A, B, C, 1.0, 0.0, trans_b=self.trans_b)
 
+    def rows_for(self, budget_flop):  # rows of the first head
+        return sample_rows(self.M, self.N, self.K, budget_flop)
+
+    def verify_launch(self, rows):
+        import torch
+        A, B, C = self.bufs[0]
+        self.launch(0)
+        torch.cuda.synchronize()
+        self.a0 = A[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        self.b0 = B[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        return C[0][torch.from_numpy(rows).cuda()].cpu().numpy()
+
+    def oracle_rows(self, rows):
+        import oracle
+        b = np.ascontiguousarray(self.b0.T) if self.trans_b else self.b0
+        ref, den = oracle.gemm(self.a0[rows], b, None, 1.0, 0.0, bf16=True)
+        return ref, den, 2.0 * len(rows) * self.N * self.K
+
+    def tolerance(self):
+        return 4e-3
+
     def kernel_name(self) -> str:
         from roofline_driven_optimisation_amd import binding
         self.launch(0)
@@ -233,6 +327,29 @@ class PreparedFp8:
         from roofline_driven_optimisation_amd import binding
         A, B, C = self.bufs[i % self.sets]
         binding.gemm_fp8(A, B, C, 1.0, 0.0, fmt=binding.FP8_E4M3)
+
+    def rows_for(self, budget_flop):
+        return sample_rows(self.M, self.N, self.K, budget_flop)
+
+    def verify_launch(self, rows):
+        import torch
+        A, B, C = self.bufs[0]
+        self.launch(0)
+        torch.cuda.synchronize()
+        self.a_host, self.b_host = A.cpu().numpy(), B.cpu().numpy()
+        return C[torch.from_numpy(rows).cuda()].cpu().numpy()
+
+    def oracle_rows(self, rows):
+        import oracle
+        ref, den = oracle.gemm_fp8(self.a_host[rows], self.b_host, None, 1.0, 0.0, 1.0, 1.0, 0)
+        return ref, den, 2.0 * len(rows) * self.N * self.K
+
+    def tolerance(self):
+        # the matrix-core kernel's summation: each group of 8 consecutive
+        # products loses under 7 * 2^-13 of its largest |product| (the
+        # instruction drops bits 13 below it), then at most 8 ceil(K / 64)
+        # + 3 fp32 roundings (the 8-bit products themselves are exact)
+        return 7 * 2.0 ** -13 + (8 * -(-self.K // 64) + 3) * 2.0 ** -23
 
     def kernel_name(self) -> str:
         from roofline_driven_optimisation_amd import binding
@@ -441,27 +558,85 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(budget_s: float = 12.0) -> dict:
-    """The CPU oracle, as it stands, timed on the leading rows of the headline
-    workload: a short calibration run sizes one sample of about budget_s."""
+# BASELINE configurations each GEMM workload belongs to (1: fp32 256^3; 2:
+# fp32 4096^3 and 4092^3; 3: bf16 4096^3; 4: LLaMA-7B prefill; 5: decode)
+CONFIG_OF = {"f32_256": 1, "f32_4096": 2, "f32_4092": 2, "bf16_4096": 3, "prefill_qkv": 4,
+             "prefill_o": 4, "prefill_gate_up": 4, "prefill_down": 4, "decode_up_m1": 5,
+             "decode_up_m8": 5, "decode_up_m16": 5, "decode_down_m1": 5, "decode_down_m8": 5,
+             "decode_down_m16": 5, "decode_lm_head": 5}
+CPU_SECONDS_PER_WORKLOAD = 1.2  # oracle time per sampled workload (the headline runs whole)
+
+
+def verify(p, seconds) -> dict:
+    """One launch outside the timed region keeps the GPU output's rows; the
+    oracle, timed on four of them, sets how many rows fit in `seconds` of
+    oracle time (all of them with an infinite budget); the operands on the
+    GPU are then freed."""
+    import torch
+    every = p.rows_for(float("inf"))
+    got = p.verify_launch(every)
+    p.bufs = None
+    if hasattr(p, "C0"):
+        p.C0 = None
+    torch.cuda.empty_cache()
+    rows = every
+    if every is not None and seconds != float("inf") and len(every) > 16:
+        t0 = time.perf_counter()
+        _, _, flop = p.oracle_rows(every[:4])
+        rate = flop / max(time.perf_counter() - t0, 1e-6)
+        rows = p.rows_for(seconds * rate)
+        got = got[rows]
+    return {"p": p, "rows": rows, "got": got}
+
+
+def cpu_leg(records) -> tuple:
+    """The CPU oracle, as it stands, on the sampled rows of every workload:
+    its time is the CPU baseline (per BASELINE configuration; configuration
+    1 also single-threaded) and its output is the reference for the parity
+    of the GPU rows kept by verify().  Returns (cpu_baseline, {workload:
+    parity})."""
     import oracle
     oracle.build(force=False)
-    w = workload(HEADLINE)
-    case = w.case()
     threads = oracle.num_threads()
-    t0 = time.perf_counter()
-    oracle.gemm(case.A[:32], case.B, None, w.alpha, 0.0, bf16=True)
-    rate = 2.0 * 32 * w.N * w.K / (time.perf_counter() - t0)
-    rows = int(max(32, min(w.M, budget_s * rate / (2.0 * w.N * w.K))))
-    t0 = time.perf_counter()
-    oracle.gemm(case.A[:rows], case.B, None, w.alpha, 0.0, bf16=True)
-    t = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "rows 0..%d of the bf16 4096^3 GEMM (%dx4096 outputs, K=4096), "
-                      "fp64 i-k-j loop, %.1f s" % (rows - 1, rows, t),
-            "cpu": cpu_model(), "logical_cpus": os.cpu_count()}
+    per, parity = [], {}
+    head = None
+    for name, rec in records:
+        p, rows = rec["p"], rec["rows"]
+        t0 = time.perf_counter()
+        ref, den, flop = p.oracle_rows(rows)
+        t = time.perf_counter() - t0
+        err = oracle.parity_error(rec["got"], ref, den)
+        tol = p.tolerance()
+        nrows = 1 if rows is None else len(rows)
+        total_rows = 1 if rows is None else (p.w.M if hasattr(p, "w") else p.M)
+        parity[name] = {"outputs_checked": int(np.size(rec["got"])),
+                        "rows": "%d of %d (leading and trailing)" % (nrows, total_rows)
+                        if rows is not None else "the sum",
+                        "err": float("%.3e" % err), "tol": float("%.3e" % tol),
+                        "ok": bool(err <= tol)}
+        entry = {"workload": name, "config": CONFIG_OF.get(name), "rows": nrows,
+                 "of_rows": total_rows, "seconds": round(t, 3),
+                 "gflops": round(flop / t / 1e9, 2), "threads": threads}
+        per.append(entry)
+        if name == HEADLINE:
+            head = entry
+        if name == "f32_256":
+            oracle.set_num_threads(1)
+            t0 = time.perf_counter()
+            p.oracle_rows(rows)
+            t1 = time.perf_counter() - t0
+            oracle.set_num_threads(threads)
+            entry["single_thread"] = {"seconds": round(t1, 4),
+                                      "gflops": round(flop / t1 / 1e9, 3), "threads": 1}
+    out = {"value": round(2.0 * head["rows"] * 4096 * 4096 / head["seconds"] / 1e12, 6),
+           "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "rows 0..%d of the bf16 4096^3 GEMM (all %d x 4096 outputs, K=4096), "
+                     "fp64 i-k-j loop, %.1f s; per_config: the oracle on sampled rows of every "
+                     "workload (%.1f s each at most)" % (head["rows"] - 1, head["rows"],
+                                                        head["seconds"],
+                                                        CPU_SECONDS_PER_WORKLOAD),
+           "per_config": per, "cpu": cpu_model(), "logical_cpus": os.cpu_count()}
+    return out, parity
 
 
 def main():
@@ -521,11 +696,16 @@ def main():
             log(json.dumps(summary(p, ev, kname)))
         return
 
+    cpu = not args.no_cpu_baseline
     log("bench: preparing %s" % HEADLINE)
     head = Prepared(HEADLINE)
     kname = head.kernel_name()
     log("bench: timing %s (%s), %d steps" % (HEADLINE, kname, args.steps))
     wall, ev = time_workload(head, args.steps, args.warmup)
+    records = []
+    head_rf = head.rf
+    if cpu:
+        records.append((HEADLINE, verify(head, float("inf"))))
 
     also = []
     for name in SECONDARY:
@@ -541,8 +721,12 @@ def main():
             s["naive_gbs"] = round(p.rf.nbytes / nsec / 1e9, 1)
         log("  " + json.dumps(s))
         also.append(s)
+        if cpu:
+            records.append((name, verify(p, CPU_SECONDS_PER_WORKLOAD)))
         del p
         torch.cuda.empty_cache()
+    if cpu:  # configuration 1 (fp32 256^3) is a parity configuration, not timed
+        records.append(("f32_256", verify(prepare("f32_256"), float("inf"))))
 
     # fused-epilogue entries: the plain GEMM of the same shape beside them
     plain = {s_["workload"]: s_["us"] for s_ in also}
@@ -566,11 +750,11 @@ def main():
         log("  " + json.dumps(ladder))
 
     traffic = stored_traffic(kname, HEADLINE)
-    achieved = head.rf.flops / ev / 1e12
+    achieved = head_rf.flops / ev / 1e12
     peak = rl.MI355X_PEAK_BF16 / 1e12
     result = {
         "metric": "GEMM TFLOP/s and % of roofline at M=N=K=4096 (fp32, bf16) + skinny-M GB/s",
-        "value": round(head.rf.flops / wall / 1e12, 2),
+        "value": round(head_rf.flops / wall / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -592,9 +776,14 @@ def main():
         "ladder": ladder,
         "page_context": PAGE_CONTEXT,
     }
-    if not args.no_cpu_baseline:
-        log("bench: CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline()
+    if cpu:
+        log("bench: CPU oracle on the sampled rows (baseline and parity)")
+        result["cpu_baseline"], parity = cpu_leg(records)
+        result["parity"] = parity.pop(HEADLINE)
+        for s_ in also:
+            s_["parity"] = parity.get(s_["workload"])
+        result["parity_f32_256"] = parity.get("f32_256")
+        log("bench: parity " + json.dumps({k: v["ok"] for k, v in parity.items()}))
     print(json.dumps(result), flush=True)
 
 

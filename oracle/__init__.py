@@ -72,6 +72,8 @@ class Oracle:
         lib.oracle_sum_f32.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         self.lib = lib
         self.path = path
 
@@ -249,6 +251,9 @@ class Oracle:
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
+    def set_num_threads(self, n: int) -> None:
+        self.lib.oracle_set_num_threads(int(n))
+
 
 _default = None
 
@@ -293,6 +298,11 @@ def gemm_batched(A, B, C=None, alpha=1.0, beta=0.0, bf16=False, trans_b=False):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use in this process."""
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later oracle calls (timing only; results do not change)."""
+    default().set_num_threads(n)
 
 
 def parity_error(c_gpu, c_ref, den) -> float:

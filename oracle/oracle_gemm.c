@@ -358,3 +358,16 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads later calls use (n >= 1); timing only,
+ * the results do not depend on it (each output is summed by one thread in
+ * ascending k). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
