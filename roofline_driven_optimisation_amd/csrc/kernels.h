@@ -60,22 +60,24 @@ const Bf16TileConfig &bf16_tile_config(int cfg);
 // `allow_split`: a 256 x 256 kernel may split its last round (see PPSplit).
 int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split);
 
-// Split of a 256 x 256 kernel's trailing tiles over K (the four-wave and the
-// ping-pong kernel share the scheme and the layout of the partials).  When the tile count
-// leaves a last round at most half full, its r tiles are each computed by two
-// workgroups, one per half of the K steps: the first posts its partial sums,
-// the second adds them and writes C, so the last round takes about half as
-// long on twice as many CUs.
+// Split of a 256 x 256 kernel's trailing tiles over K (the four-wave, the
+// ping-pong and the 8-bit float kernel share the scheme and the layout of
+// the partials).  When the tile count leaves a last round at most half full,
+// its r tiles are each computed by two workgroups, one per part of the K
+// steps: the first posts its partial sums, the second adds them and writes
+// C, so the last round takes about half as long on twice as many CUs.
 //
-// The pair's handshake.  When a workgroup of a pair has finished its K
-// steps, one thread swaps the epoch into the tile's claim word: the first to
-// arrive (old value != epoch) posts its partial tile and then publishes the
-// epoch in the tile's flag with a release store; the second waits for the
-// flag with an acquire, adds the partial to its own sums and writes C.  The
-// second thus only ever waits for a workgroup that is already past its K
-// loop, whatever order the workgroups were dispatched in.  The wait is
-// bounded by poll_limit flag reads; a wait that gives up writes NaN into its
-// tile and adds one to *timeouts, which the host can read back.
+// The pair's handshake.  When a workgroup of a pair starts, one thread swaps
+// the epoch into the tile's claim word: the first to claim (old value !=
+// epoch) becomes split 0, takes the first split_step K steps, posts its
+// partial tile and then publishes the epoch in the tile's flag with a
+// release store; the other becomes split 1, takes the remaining steps,
+// waits for the flag with an acquire, adds the partial to its own sums and
+// writes C.  The waiting workgroup thus only ever waits for one that is
+// already running and never waits itself, whatever order the workgroups
+// were dispatched in.  The wait is bounded by poll_limit flag reads; a wait
+// that gives up writes NaN into its tile and adds one to *timeouts, which
+// the host can read back.
 constexpr int kPPTile = 256;  // the square tile of both 256 x 256 kernels
 constexpr int kPollLimitDefault = 1 << 22;  // flag reads, about 0.5 s
 struct PPSplit {
