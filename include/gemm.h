@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 6
+#define GEMM_ABI_VERSION 7
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -96,7 +96,8 @@ enum gemm_status {
     GEMM_ERR_INVALID_ARG = 1,
     GEMM_ERR_LAUNCH = 2,
     GEMM_ERR_ALLOC = 3,
-    GEMM_ERR_DEVICE = 4
+    GEMM_ERR_DEVICE = 4,
+    GEMM_ERR_SCRATCH = 5  /* gemm_bf16_noalloc: the call needs more than its fixed scratch */
 };
 
 /*
@@ -115,6 +116,33 @@ GEMM_API int gemm_f32(int M, int N, int K, float alpha, float beta,
  */
 GEMM_API int gemm_bf16(int M, int N, int K, float alpha, float beta,
               const uint16_t *A, const uint16_t *B, float *C, void *stream);
+
+/*
+ * gemm_bf16 for callers that cannot allocate device memory: code running
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layouts, semantics and error behaviour as
+ * gemm_bf16; this entry point calls no hipMalloc, hipFree or allocating
+ * library routine.  Its only scratch is a fixed 8 MiB array in the
+ * library's device code (one per GPU, held until the process ends): the
+ * decode-shaped kernel (M <= 16) splits K through it, with every column
+ * block's partial sums kept inside one XCD; other shapes run the tiled
+ * kernel on whole tiles (no split of a last round).  A decode-shaped call
+ * whose split would need more than the array holds returns GEMM_ERR_SCRATCH
+ * and launches nothing: each XCD's 1 MiB share keeps 64 KiB of counters and
+ * the fp32 partial sums of its ceil(N / 1024) column blocks of 128, so it
+ * takes ceil(N / 1024) * splits * M <= 1920 (the decode shapes split K
+ * eight ways: N = 11008 at M = 16 uses 1408; N = 16384 at M = 16 is
+ * refused).
+ * The first call on a device that is not under graph capture clears the
+ * array's counters and, if no gemm_bf16 call has done so yet, runs the XCD
+ * dealing probe (both on the caller's stream, waiting for the probe);
+ * before that, and on a device that does not deal workgroups round-robin,
+ * decode-shaped calls run in one split.  Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams, or
+ * host threads) race and must be serialised by the caller.
+ */
+GEMM_API int gemm_bf16_noalloc(int M, int N, int K, float alpha, float beta,
+                               const uint16_t *A, const uint16_t *B, float *C, void *stream);
 
 /*
  * Fused Linear-layer epilogue.  A Linear layer computes Y = XW + b (page

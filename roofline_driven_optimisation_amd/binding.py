@@ -49,7 +49,8 @@ def library():
                 % path)
         lib = ctypes.CDLL(path)
         i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
-        for name in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16"):
+        for name in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16",
+                     "gemm_bf16_noalloc"):
             fn = getattr(lib, name)
             fn.argtypes = [i, i, i, f, f, vp, vp, vp, vp]
             fn.restype = ctypes.c_int
@@ -187,6 +188,13 @@ def gemm_bf16(A, B, C, alpha=1.0, beta=0.0, stream=None):
     """C = alpha*A@B + beta*C with bfloat16 A and B, float32 C."""
     import torch
     return _call("gemm_bf16", A, B, C, alpha, beta, stream, torch.bfloat16)
+
+
+def gemm_bf16_noalloc(A, B, C, alpha=1.0, beta=0.0, stream=None):
+    """gemm_bf16 that allocates nothing: its scratch is the library's fixed
+    per-GPU array (GemmError with status 5 when the call needs more)."""
+    import torch
+    return _call("gemm_bf16_noalloc", A, B, C, alpha, beta, stream, torch.bfloat16)
 
 
 def gemm_f32_bias_act(A, B, C, bias=None, activation=ACT_NONE, alpha=1.0, beta=0.0,

@@ -161,18 +161,21 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
 // (cached) device memory: `xcd_base` is kXcdCount blocks of kSkinnyXcdBytes,
 // block x touched only by the workgroups with blockIdx % 8 == x, each holding
 // kSkinnyXcdCounterInts counters (zero on entry and left zero on exit) and
-// then the partial sums.  The remaining col_blocks % 8 column blocks reduce
-// through `partials` and `counters` as in launch_skinny_bf16.
+// then the partial sums (xcd_block_bytes per block in all).  The remaining
+// col_blocks % 8 column blocks reduce through `partials` and `counters` as
+// in launch_skinny_bf16, unless all_local: then those blocks are XCD-local
+// too (some XCDs get one block more, the grid is padded with workgroups
+// that exit at once) and `partials` and `counters` are not used.
 // skinny_xcd_local_fits says whether a shape may use this form.
 constexpr int kXcdCount = 8;
 constexpr size_t kSkinnyXcdBytes = size_t(4) << 20;
 constexpr int kSkinnyXcdCounterInts = 16384;
-bool skinny_xcd_local_fits(int M, int N, int K, int splits);
+bool skinny_xcd_local_fits(int M, int N, int K, int splits, size_t block_bytes, bool all_local);
 hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
                                   const uint16_t *A, const uint16_t *B, float *C, int splits,
                                   float *partials, int *counters, int counter_ints,
-                                  char *xcd_base, int xcd_group, const Epi &epi,
-                                  hipStream_t stream);
+                                  char *xcd_base, size_t xcd_block_bytes, int xcd_group,
+                                  bool all_local, const Epi &epi, hipStream_t stream);
 // Sum of a float32 vector (4-byte aligned, any length) into *out, on the
 // device.  blocks <= kReduceMaxBlocks workgroups each stream a contiguous
 // chunk; with blocks > 1 they reduce through `partials` (blocks floats) and
@@ -190,7 +193,10 @@ hipError_t launch_reduce_sum_tree(const float *x, long long n, float *out, float
 // Runs a probe grid on `stream`, waits for it, and sets *ok when every
 // workgroups whose ids are equal modulo kXcdCount ran on one XCD and the
 // kXcdCount residues on different XCDs (which XCD takes workgroup 0 varies
-// between launches and is not checked).
-hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream);
+// between launches and is not checked).  The grid writes kXcdProbeInts ints
+// into `buffer` (device memory the caller owns), or into a block the
+// function allocates and frees when `buffer` is null.
+constexpr int kXcdProbeInts = 4096;
+hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream, int *buffer = nullptr);
 
 }  // namespace mgemm

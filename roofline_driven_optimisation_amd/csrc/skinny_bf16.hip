@@ -103,9 +103,12 @@ struct Stage {
 // (counted from the end of that first part) is split j % splits of the
 // (j / splits)-th of the q column blocks given to XCD x: runs of xcd_group
 // adjacent blocks, dealt to the groups in turn.  Group x uses only the
-// scratch block at xcd_base + x * kSkinnyXcdBytes (counters first, then the partials
-// of its column blocks, 128 columns wide), so that part of the reduction
-// stays in one XCD's L2.  Every XCD gets the same number of workgroups.
+// scratch block at xcd_base + x * xcd_block_bytes (counters first, then the
+// partials of its column blocks, 128 columns wide), so that part of the
+// reduction stays in one XCD's L2.  Every XCD gets the same number of
+// workgroups.  With all_local, r = 0 and q = ceil(col_blocks / 8): the
+// placement is the same, and a workgroup whose block number comes out at or
+// past col_blocks (the padding of the last round) exits at once.
 template <bool XCD_LOCAL, bool EPI>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, float alpha,
                                                           float beta,
@@ -114,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
                                                           float *C, int splits, int kblk_per_split,
                                                           float *partials, int *counters,
                                                           int counter_stride, char *xcd_base,
-                                                          int xcd_group, Epi epi) {
+                                                          long long xcd_block_bytes, int xcd_group,
+                                                          int all_local, Epi epi) {
     __shared__ f32x4 red[kWaves][8][64];
     __shared__ int s_last;
 
@@ -122,7 +126,10 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
     bool local = false;  // uniform over the workgroup
     if (XCD_LOCAL) {
         const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
-        const int rest = col_blocks % kXcdCount;
+        // all_local: every column block is XCD-local, the last round of
+        // blocks padded with idle workgroups; otherwise col_blocks % 8
+        // blocks reduce through uncached memory
+        const int rest = all_local ? 0 : col_blocks % kXcdCount;
         const int rest_groups = (rest * splits + kXcdCount - 1) / kXcdCount * kXcdCount;
         const int b = blockIdx.x;
         if (b < rest_groups) {
@@ -136,14 +143,17 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int M, int N, int K, f
             cb_local = j / splits;
             sp = j - cb_local * splits;
             {
-                const int q = col_blocks / kXcdCount, g = xcd_group;
+                const int q = all_local ? (col_blocks + kXcdCount - 1) / kXcdCount
+                                        : col_blocks / kXcdCount;
+                const int g = xcd_group;
                 const int full = (q / g) * g;
                 if (cb_local < full)
                     cb = (cb_local / g) * kXcdCount * g + x * g + cb_local % g;
                 else
                     cb = full * kXcdCount + x * (q - full) + (cb_local - full);
             }
-            char *blk = xcd_base + static_cast<size_t>(x) * kSkinnyXcdBytes;
+            if (cb >= col_blocks) return;  // all_local padding: exits before any barrier
+            char *blk = xcd_base + static_cast<size_t>(x) * xcd_block_bytes;
             counters = reinterpret_cast<int *>(blk);
             counter_stride = kCounterLine;
             partials = reinterpret_cast<float *>(blk + kSkinnyXcdCounterInts * sizeof(int));
@@ -417,11 +427,11 @@ hipError_t launch_skinny_bf16(int M, int N, int K, float alpha, float beta, cons
     if (epi_on(epi))
         skinny_kernel<false, true><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
                                                           real_splits, per, partials, counters,
-                                                          counter_stride, nullptr, 1, epi);
+                                                          counter_stride, nullptr, 0, 1, 0, epi);
     else
         skinny_kernel<false, false><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
                                                            real_splits, per, partials, counters,
-                                                           counter_stride, nullptr, 1, epi);
+                                                           counter_stride, nullptr, 0, 1, 0, epi);
     return hipGetLastError();
 }
 
@@ -446,12 +456,12 @@ __global__ __launch_bounds__(256) void xcd_probe_kernel(int *xcc, int count) {
 
 }  // namespace
 
-hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream) {
+hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream, int *buffer) {
     *ok = false;
-    constexpr int kProbeGroups = 4096;
-    int *d = nullptr;
-    hipError_t e = hipMalloc(&d, kProbeGroups * sizeof(int));
-    if (e != hipSuccess) return e;
+    constexpr int kProbeGroups = kXcdProbeInts;
+    int *d = buffer;
+    hipError_t e = hipSuccess;
+    if (d == nullptr && (e = hipMalloc(&d, kProbeGroups * sizeof(int))) != hipSuccess) return e;
     static int h[kProbeGroups];
     static std::mutex mu;
     std::lock_guard<std::mutex> lock(mu);
@@ -459,7 +469,7 @@ hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream) {
     e = hipGetLastError();
     if (e == hipSuccess) e = hipMemcpyAsync(h, d, sizeof(h), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
-    (void)hipFree(d);
+    if (buffer == nullptr) (void)hipFree(d);
     if (e != hipSuccess) return e;
     // The XCD of workgroup 0 varies between launches (the dispatcher's
     // round robin can carry over from earlier work); what the kernels rely
@@ -476,24 +486,29 @@ hipError_t probe_xcd_mapping(bool *ok, hipStream_t stream) {
     return hipSuccess;
 }
 
-bool skinny_xcd_local_fits(int M, int N, int K, int splits) {
+bool skinny_xcd_local_fits(int M, int N, int K, int splits, size_t block_bytes, bool all_local) {
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
     const int per = (kblks + splits - 1) / splits > 0 ? (kblks + splits - 1) / splits : 1;
     const int real_splits = (kblks + per - 1) / per;
-    const int mine = col_blocks / kXcdCount;  // XCD-local column blocks per XCD
+    // XCD-local column blocks per XCD
+    const int mine = all_local ? (col_blocks + kXcdCount - 1) / kXcdCount : col_blocks / kXcdCount;
     if (real_splits < 2 || M < 1 || M > kSkinnyMaxM || mine < 1) return false;
     if (mine * kCounterLine > kSkinnyXcdCounterInts) return false;
-    return static_cast<long long>(mine) * real_splits * M * kSkinnyCols * sizeof(float) <=
-           static_cast<long long>(kSkinnyXcdBytes - kSkinnyXcdCounterInts * sizeof(int));
+    const size_t head = kSkinnyXcdCounterInts * sizeof(int);
+    return block_bytes > head &&
+           static_cast<unsigned long long>(mine) * real_splits * M * kSkinnyCols * sizeof(float) <=
+               block_bytes - head;
 }
 
 hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
                                   const uint16_t *A, const uint16_t *B, float *C, int splits,
                                   float *partials, int *counters, int counter_ints,
-                                  char *xcd_base, int xcd_group, const Epi &epi,
-                                  hipStream_t stream) {
-    if (xcd_base == nullptr || !skinny_xcd_local_fits(M, N, K, splits)) return hipErrorInvalidValue;
+                                  char *xcd_base, size_t xcd_block_bytes, int xcd_group,
+                                  bool all_local, const Epi &epi, hipStream_t stream) {
+    if (xcd_base == nullptr ||
+        !skinny_xcd_local_fits(M, N, K, splits, xcd_block_bytes, all_local))
+        return hipErrorInvalidValue;
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
     const int per = (kblks + splits - 1) / splits;
@@ -501,25 +516,31 @@ hipError_t launch_skinny_bf16_xcd(int M, int N, int K, float alpha, float beta,
         static_cast<long long>(M) * K * 2 >= 0x7fff0000LL)
         return hipErrorInvalidValue;
     const int real_splits = (kblks + per - 1) / per;
-    const int rest = col_blocks % kXcdCount;
+    const int rest = all_local ? 0 : col_blocks % kXcdCount;
     if (rest > 0 && (partials == nullptr || counters == nullptr || col_blocks > counter_ints))
         return hipErrorInvalidValue;
     const int counter_stride = col_blocks * kCounterLine <= counter_ints ? kCounterLine : 1;
     const long long rest_groups =
         (static_cast<long long>(rest) * real_splits + kXcdCount - 1) / kXcdCount * kXcdCount;
-    const long long grid =
-        rest_groups + static_cast<long long>(col_blocks - rest) * real_splits;
+    const long long local_blocks =
+        all_local ? static_cast<long long>((col_blocks + kXcdCount - 1) / kXcdCount) * kXcdCount
+                  : col_blocks - rest;
+    const long long grid = rest_groups + local_blocks * real_splits;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
     const int grp = xcd_group < 1 ? 1 : xcd_group;
+    const long long bb = static_cast<long long>(xcd_block_bytes);
+    const int al = all_local ? 1 : 0;
     if (epi_on(epi))
         skinny_kernel<true, true><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
                                                          real_splits, per, partials, counters,
-                                                         counter_stride, xcd_base, grp, epi);
+                                                         counter_stride, xcd_base, bb, grp, al,
+                                                         epi);
     else
         skinny_kernel<true, false><<<g, blk, 0, stream>>>(M, N, K, alpha, beta, A, B, C,
                                                           real_splits, per, partials, counters,
-                                                          counter_stride, xcd_base, grp, epi);
+                                                          counter_stride, xcd_base, bb, grp, al,
+                                                          epi);
     return hipGetLastError();
 }
 
