@@ -1333,9 +1333,13 @@ int tile_lds_bytes(int c) {
 // (l % 32) for both operands (checked on the device against a host
 // product); it does four times the work of the bf16 32x32x16 MFMA at the
 // 8-bit rate, so a step is 16 MFMAs per wave instead of 32.  Schedule: the
-// fragments of step t (two 16-byte reads each) are read while the last 8
-// MFMAs of step t - 1 run, the copies of step t + 3 go out with the first
-// 8 MFMAs of step t, then one wait and one barrier, as in the bf16 kernel.
+// fragments the first 8 MFMAs of step t use (two 16-byte reads each) are
+// read while the last 8 MFMAs of step t - 1 run, the other two during step
+// t's first 8, with the copies of step t + 3; then one wait and one
+// barrier, as in the bf16 kernel.  Fragments alternate between two register
+// buffers step by step; every step instance is compiled with its buffer and
+// its copy flag fixed (see the loop), so the 256 accumulators stay in
+// AccVGPRs and nothing spills.
 template <bool KTAIL, int FMT>
 __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, float alpha,
                                                         float beta,
@@ -1463,46 +1467,57 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
     __syncthreads();
     using Even = std::integral_constant<int, 0>;
     using Odd = std::integral_constant<int, 1>;
-#pragma unroll
-    for (int o = 0; o < kPairs; ++o) read_pair(0, o, Even());
 
-    // the fragment buffer is t % 2: each parity is compiled separately so
-    // that the fragment arrays are indexed statically (kept in registers)
+    // Each step alternates between the two fragment buffers, and whether it
+    // issues copies is a compile-time flag, so every instance of the step
+    // below indexes its fragment arrays statically and holds no branch
+    // between its MFMAs (a runtime copy flag split the MFMA chains into
+    // blocks, and the register allocator then moved an accumulator through
+    // VGPRs on every step).  The buffer of step t is (t + copy_end) % 2: the
+    // copying steps run in one of two loops, picked once by the parity of
+    // copy_end, and both leave the same state for the S - 1 = 3 steps that
+    // copy nothing, written out straight (choosing among step variants at
+    // run time inside a loop spilled).
     const int copy_end = max(0, T - (S - 1));
-    auto k_step = [&](int t, auto buf_tag) {
-        const bool copy = t < copy_end;  // uniform
+    auto k_step = [&](int t, auto buf_tag, auto copy_tag, auto tail_tag) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        constexpr bool TAIL = decltype(tail_tag)::value;  // false for step 0 only
         constexpr int buf = decltype(buf_tag)::value;
         const int cur = t % S;
         using Cur = std::integral_constant<int, buf>;
         using Prev = std::integral_constant<int, buf ^ 1>;
-        if (t > 0) {
+        // The fragments the first eight MFMAs use (B blocks 0 and 1, every A
+        // block: read pairs 0 .. 5) are read under the previous step's last
+        // eight; B blocks 2 and 3 (pairs 6, 7), used only by this step's
+        // last eight, under this step's first eight, so that the LDS reads
+        // are spread over the whole step instead of half of it.
+        constexpr int kFirstReads = kPairs - 2;
+        if constexpr (TAIL) {
 #pragma unroll
             for (int q = 0; q < kTail; ++q) {
                 mfma(kEarly + q, Prev());
-                read_pair(cur, q, Cur());
+                if (q < kFirstReads) read_pair(cur, q, Cur());
                 __builtin_amdgcn_sched_barrier(0);
             }
+        } else {  // step 0: its first fragments are read here, with no MFMA to hide them
+#pragma unroll
+            for (int q = 0; q < kFirstReads; ++q) read_pair(cur, q, Cur());
         }
-        const StepCopy next = step_copy(copy ? t + S - 1 : t);
+        StepCopy next;
+        if constexpr (COPY) next = step_copy(t + S - 1);
 #pragma unroll
         for (int q = 0; q < kEarly; ++q) {
             mfma(q, Cur());
-            if (copy) issue_copy(next, q);
+            if (q == 1 || q == 4) read_pair(cur, kFirstReads + (q == 4), Cur());
+            if constexpr (COPY) issue_copy(next, q);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (copy)
-            __builtin_amdgcn_s_waitcnt(kWaitSteady);
-        else
-            __builtin_amdgcn_s_waitcnt(kWaitDrain);
+        __builtin_amdgcn_s_waitcnt(COPY ? kWaitSteady : kWaitDrain);
         __syncthreads();
     };
-    // two steps per iteration, so that each step's fragment buffer is fixed
-    int t = 0;
-    for (; t + 1 < T; t += 2) {
-        k_step(t, Even());
-        k_step(t + 1, Odd());
-    }
-    if (t < T) k_step(t, Even());
+    using On = std::true_type;
+    using Off = std::false_type;
+    static_assert(S == 4, "three steps follow the last copying step");
     auto last = [&](auto buf_tag) {
 #pragma unroll
         for (int q = 0; q < kTail; ++q) {
@@ -1510,8 +1525,37 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if ((T - 1) & 1) last(Odd());
-    else last(Even());
+    if (copy_end > 0) {
+        int t = 1;
+        if (copy_end & 1) {  // step 0 in buffer 1
+            k_step(0, Odd(), On(), Off());
+            for (; t < copy_end; t += 2) {
+                k_step(t, Even(), On(), On());
+                k_step(t + 1, Odd(), On(), On());
+            }
+        } else {  // step 0 in buffer 0, an odd number of copying steps after it
+            k_step(0, Even(), On(), Off());
+            for (; t + 1 < copy_end; t += 2) {
+                k_step(t, Odd(), On(), On());
+                k_step(t + 1, Even(), On(), On());
+            }
+            k_step(t, Odd(), On(), On());
+            ++t;
+        }
+        // t == copy_end, in buffer 0
+        k_step(t, Even(), Off(), On());
+        k_step(t + 1, Odd(), Off(), On());
+        k_step(t + 2, Even(), Off(), On());
+        last(Even());
+    } else {  // T <= 3: no step issues copies
+        k_step(0, Even(), Off(), Off());
+        if (T > 1) k_step(1, Odd(), Off(), On());
+        if (T > 2) k_step(2, Even(), Off(), On());
+        if ((T - 1) & 1)
+            last(Odd());
+        else
+            last(Even());
+    }
 
     // epilogue: as the bf16 kernel's, each wave staging through a private
     // 16 KB slice of the A stages
