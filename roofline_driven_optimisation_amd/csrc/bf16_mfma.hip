@@ -1335,8 +1335,9 @@ int tile_lds_bytes(int c) {
 // 8-bit rate, so a step is 16 MFMAs per wave instead of 32.  Schedule: the
 // fragments the first 8 MFMAs of step t use (two 16-byte reads each) are
 // read while the last 8 MFMAs of step t - 1 run, the other two during step
-// t's first 8, with the copies of step t + 3; then one wait and one
-// barrier, as in the bf16 kernel.  Fragments alternate between two register
+// t's first 8; the copies of step t + 3 go out one per two MFMAs over all
+// 16 (a burst of them in half the step was 3.5 % slower); then one wait and
+// one barrier, as in the bf16 kernel.  Fragments alternate between two register
 // buffers step by step; every step instance is compiled with its buffer and
 // its copy flag fixed (see the loop), so the 256 accumulators stay in
 // AccVGPRs and nothing spills.
@@ -1491,25 +1492,37 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
         // eight; B blocks 2 and 3 (pairs 6, 7), used only by this step's
         // last eight, under this step's first eight, so that the LDS reads
         // are spread over the whole step instead of half of it.
+        // The copies of step t + 3 fill the stage step t - 1 used, whose
+        // last fragments were read before the previous barrier: they go out
+        // one per two MFMAs over the whole step (a burst of them delays the
+        // MFMAs behind the copy queue).
         constexpr int kFirstReads = kPairs - 2;
+        StepCopy next;
+        if constexpr (COPY) next = step_copy(t + S - 1);
         if constexpr (TAIL) {
 #pragma unroll
             for (int q = 0; q < kTail; ++q) {
                 mfma(kEarly + q, Prev());
                 if (q < kFirstReads) read_pair(cur, q, Cur());
+                if constexpr (COPY) {
+                    if (q & 1) issue_copy(next, q >> 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {  // step 0: its first fragments are read here, with no MFMA to hide them
 #pragma unroll
             for (int q = 0; q < kFirstReads; ++q) read_pair(cur, q, Cur());
         }
-        StepCopy next;
-        if constexpr (COPY) next = step_copy(t + S - 1);
 #pragma unroll
         for (int q = 0; q < kEarly; ++q) {
             mfma(q, Cur());
             if (q == 1 || q == 4) read_pair(cur, kFirstReads + (q == 4), Cur());
-            if constexpr (COPY) issue_copy(next, q);
+            if constexpr (COPY) {
+                if (!TAIL)
+                    issue_copy(next, q);
+                else if (q & 1)
+                    issue_copy(next, COPIES / 2 + (q >> 1));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(COPY ? kWaitSteady : kWaitDrain);
