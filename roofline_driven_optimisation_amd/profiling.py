@@ -33,6 +33,8 @@ KERNEL_SOURCES = {
     "f32_dma": "f32_mfma.hip",
     "skinny": "skinny_bf16.hip",
     "naive": "naive.hip",
+    "fp8_q4": "bf16_mfma.hip",
+    "reduce": "reduce.hip",
 }
 
 
@@ -85,17 +87,29 @@ def kernel_stats(path: str):
     return rows
 
 
-def dispatch_stats(path: str):
-    """Per (kernel, grid size) statistics from a ``*_kernel_trace.csv``: one
-    kernel launched on several shapes shows up once per launch shape."""
-    acc = defaultdict(list)
+def dispatch_stats(path: str, last: int = 0):
+    """Statistics from a ``*_kernel_trace.csv``, one row per run of
+    consecutive dispatches of one kernel with one launch shape (a benchmark
+    times its workloads one after another, so two workloads that launch the
+    same kernel on the same grid still come out as separate rows, in time
+    order).  With ``last`` > 0 only runs of at least ``last`` dispatches are
+    reported, each by its last ``last`` dispatches: the timed, steady-state
+    launches of each workload, not the warm-up or the copies between them."""
     with open(path) as f:
-        for r in csv.DictReader(f):
-            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
-            acc[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    total = sum(sum(v) for v in acc.values())
+        rows_in = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in rows_in:
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(us)
+        else:
+            runs.append((key, [us]))
+    if last > 0:
+        runs = [(k, v[-last:]) for k, v in runs if len(v) >= last]
+    total = sum(sum(v) for _, v in runs)
     rows = []
-    for (k, grid, wg), v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+    for (k, grid, wg), v in runs:
         rows.append({"kernel": "%s [%d workgroups x %d]" % (k, grid // max(wg, 1), wg),
                      "calls": len(v), "avg_us": statistics.mean(v), "min_us": min(v),
                      "max_us": max(v), "pct": 100.0 * sum(v) / total})
@@ -115,49 +129,55 @@ def counter_medians(path: str):
     return {k: statistics.median(v) for k, v in acc.items()}
 
 
-NUM_XCD = 8          # GRBM counters are summed over the XCDs
 NUM_SIMD = 256 * 4   # MFMA busy cycles are summed over every SIMD
 SPEC_CLOCK_GHZ = 2.4
 MOPS_FLOP = 512      # one MFMA "MOP" is 512 floating-point operations
 
 
-def mfma_rows(path: str):
-    """Per kernel and launch shape, from one --pmc pass with GRBM_GUI_ACTIVE,
-    SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_* (medians over
-    dispatches): duration, average shader clock, share of SIMD cycles the
-    matrix cores were busy, and the MFMA FLOPs counted."""
+def mfma_rows(path: str, last: int = 0):
+    """Per kernel and launch shape, from one --pmc pass with
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_* (BF16, F8, F32),
+    SQ_WAVE_CYCLES, SQ_WAIT_INST_ANY and SQ_WAIT_INST_LDS (medians over the
+    last ``last`` dispatches, all if 0): the dispatch time, the MFMA FLOPs
+    counted, the matrix cores' busy cycles per SIMD, and the share of wave
+    cycles spent waiting (on any dependency; on LDS).  The shader clock is
+    not derived from counters here: the steady-state clock comes from
+    amd-smi samples (bench.py --sustain)."""
     acc = defaultdict(lambda: defaultdict(list))
     with open(path) as f:
-        for r in csv.DictReader(f):
-            wg = max(int(r.get("Workgroup_Size", 1) or 1), 1)
-            grid = int(r.get("Grid_Size", 0) or 0)
-            name = "%s [%d workgroups]" % (short_name(r["Kernel_Name"]), grid // wg)
-            acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
-            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
-                acc[name]["_ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        rows_in = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows_in:
+        wg = max(int(r.get("Workgroup_Size", 1) or 1), 1)
+        grid = int(r.get("Grid_Size", 0) or 0)
+        name = "%s [%d workgroups]" % (short_name(r["Kernel_Name"]), grid // wg)
+        acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "SQ_WAVE_CYCLES":
+            acc[name]["_ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     rows = []
     for name, c in sorted(acc.items()):
-        if "GRBM_GUI_ACTIVE" not in c or not any(c["SQ_VALU_MFMA_BUSY_CYCLES"]):
+        if not any(c.get("SQ_VALU_MFMA_BUSY_CYCLES", [])):
             continue
-        med = {k: statistics.median(v) for k, v in c.items()}
-        cycles = med["GRBM_GUI_ACTIVE"] / NUM_XCD
-        ns = med["_ns"]
+        if last > 0:
+            c = {k: v[-last:] for k, v in c.items()}
+        med = {k: statistics.median(v) for k, v in c.items() if v}
         mops = sum(v for k, v in med.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
-        rows.append({"kernel": name, "us": ns / 1e3, "clock_ghz": cycles / ns,
-                     "mfma_busy": med["SQ_VALU_MFMA_BUSY_CYCLES"] / (NUM_SIMD * cycles),
+        wave = med.get("SQ_WAVE_CYCLES", float("nan"))
+        rows.append({"kernel": name, "us": med["_ns"] / 1e3,
                      "mfma_gflop": mops * MOPS_FLOP / 1e9,
-                     "mfma_tflops": mops * MOPS_FLOP / ns / 1e3})
+                     "busy_per_simd": med["SQ_VALU_MFMA_BUSY_CYCLES"] / NUM_SIMD,
+                     "wait_any": med.get("SQ_WAIT_INST_ANY", float("nan")) / wave,
+                     "wait_lds": med.get("SQ_WAIT_INST_LDS", float("nan")) / wave})
     return rows
 
 
 def mfma_markdown(rows) -> str:
-    out = ["| kernel | us | avg clock GHz | MFMA busy (of SIMD cycles) | MFMA GFLOP counted | "
-           "TFLOP/s from counters | share of spec (busy x clock / 2.4 GHz) |",
-           "|---|---|---|---|---|---|---|"]
+    out = ["| kernel | us (under counters) | MFMA GFLOP counted | MFMA busy cycles per SIMD | "
+           "wave cycles waiting (any) | wave cycles waiting (LDS) |",
+           "|---|---|---|---|---|---|"]
     for r in rows:
-        out.append("| %s | %.1f | %.2f | %.1f %% | %.1f | %.1f | %.1f %% |" % (
-            r["kernel"], r["us"], r["clock_ghz"], 100 * r["mfma_busy"], r["mfma_gflop"],
-            r["mfma_tflops"], 100 * r["mfma_busy"] * r["clock_ghz"] / SPEC_CLOCK_GHZ))
+        out.append("| %s | %.1f | %.1f | %.0f | %.1f %% | %.1f %% |" % (
+            r["kernel"], r["us"], r["mfma_gflop"], r["busy_per_simd"], 100 * r["wait_any"],
+            100 * r["wait_lds"]))
     return "\n".join(out)
 
 
@@ -185,9 +205,14 @@ def main():
     t = sub.add_parser("trace", help="markdown table per kernel and launch shape from "
                        "--kernel-trace output")
     t.add_argument("dir")
-    m = sub.add_parser("mfma", help="clock and matrix-core utilisation from a --pmc pass "
-                       "with GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_*")
+    t.add_argument("--last", type=int, default=0,
+                   help="report runs of at least N consecutive dispatches by their last N "
+                   "(steady state)")
+    m = sub.add_parser("mfma", help="matrix-core work and wave waits from a --pmc pass "
+                       "with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_*, SQ_WAVE_CYCLES, "
+                       "SQ_WAIT_INST_ANY, SQ_WAIT_INST_LDS")
     m.add_argument("dir")
+    m.add_argument("--last", type=int, default=0)
     c = sub.add_parser("counters", help="calibrated HBM bytes per dispatch")
     c.add_argument("--fetch", required=True, help="dir of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="dir of the WRITE_SIZE run")
@@ -199,10 +224,10 @@ def main():
         print(stats_markdown(kernel_stats(_find(args.dir, "_kernel_stats.csv"))))
         return
     if args.cmd == "mfma":
-        print(mfma_markdown(mfma_rows(_find(args.dir, "_counter_collection.csv"))))
+        print(mfma_markdown(mfma_rows(_find(args.dir, "_counter_collection.csv"), args.last)))
         return
     if args.cmd == "trace":
-        print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"))))
+        print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"), args.last)))
         return
     fetch = counter_medians(_find(args.fetch, "_counter_collection.csv"))
     write = counter_medians(_find(args.write, "_counter_collection.csv"))

@@ -21,3 +21,39 @@ def test_source_hash_known_families():
         assert len(h) == 16 and int(h, 16) >= 0
     assert source_hash("bf16_q4") == source_hash("bf16_pp")  # one source file
     assert source_hash("unknown_kernel") == ""
+    assert source_hash("fp8_q4") == source_hash("bf16_q4")
+    assert len(source_hash("reduce")) == 16
+
+
+def _trace_csv(path, dispatches):
+    """A minimal kernel-trace CSV: (name, grid, workgroup, start ns, end ns)."""
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp",
+                    "End_Timestamp"])
+        for d in dispatches:
+            w.writerow(d)
+
+
+def test_dispatch_stats_splits_runs_of_one_kernel(tmp_path):
+    """Two workloads that launch the same kernel on the same grid, with a copy
+    between them, come out as two rows in time order; --last keeps the tail
+    of each long run and drops short runs."""
+    from roofline_driven_optimisation_amd.profiling import dispatch_stats
+    k = "void gemm_kernel<true>(float*) [clone .kd]"
+    rows, t = [], 0
+    for us in [9.0] * 2 + [4.0] * 5:  # warm-up then steady state, workload 1
+        rows.append((k, 65536, 256, t, t + int(us * 1000))); t += 20000
+    rows.append(("__amd_rocclr_copyBuffer", 1024, 512, t, t + 1000)); t += 20000
+    for us in [8.0] * 5:             # workload 2, same kernel and grid
+        rows.append((k, 65536, 256, t, t + int(us * 1000))); t += 20000
+    rows.sort(key=lambda r: -r[3])  # the file's own order does not matter
+    path = tmp_path / "t_kernel_trace.csv"
+    _trace_csv(path, rows)
+    all_runs = dispatch_stats(str(path))
+    assert [r["calls"] for r in all_runs] == [7, 1, 5]
+    steady = dispatch_stats(str(path), last=5)
+    assert [r["calls"] for r in steady] == [5, 5]
+    assert [r["avg_us"] for r in steady] == [4.0, 8.0]
+    assert steady[0]["kernel"] == steady[1]["kernel"] == "gemm_kernel<true> [256 workgroups x 256]"
