@@ -610,7 +610,8 @@ def cpu_leg(records) -> tuple:
         nrows = 1 if rows is None else len(rows)
         total_rows = 1 if rows is None else (p.w.M if hasattr(p, "w") else p.M)
         parity[name] = {"outputs_checked": int(np.size(rec["got"])),
-                        "rows": "%d of %d (leading and trailing)" % (nrows, total_rows)
+                        "rows": ("all %d" % total_rows if nrows == total_rows else
+                                 "%d of %d (leading and trailing)" % (nrows, total_rows))
                         if rows is not None else "the sum",
                         "err": float("%.3e" % err), "tol": float("%.3e" % tol),
                         "ok": bool(err <= tol)}

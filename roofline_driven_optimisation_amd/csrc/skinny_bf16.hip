@@ -12,10 +12,12 @@
 // (N / 128) * splits workgroups.  One CU alone cannot keep enough loads in
 // flight to draw more than a few tens of GB/s, so the grid is sized to a few
 // workgroups per CU over all 256 CUs.  Inside a workgroup the waves take
-// turns over 32-row k-blocks.  The loop is software-pipelined two k-blocks
-// deep: the sixteen 16-byte loads of the next pair of k-blocks are issued
-// before the current pair is multiplied, so every lane keeps 16 to 32 loads
-// in flight the whole time, not just between compute bursts.
+// turns over 32-row k-blocks.  The loop is software-pipelined one k-block
+// deep: the eight 16-byte B loads (and the A load) of a wave's next k-block
+// are issued before its current k-block is multiplied, so every lane keeps
+// 8 to 16 loads in flight the whole time, not just between compute bursts.
+// At that depth a wave needs few enough registers for three workgroups per
+// CU, which keeps more loads in flight per CU than a deeper pipeline at two.
 //
 // Per k-block, lane l loads eight B rows (k = 32 kb + 8 (l / 16) + e) at
 // columns 8 (l % 16) .. +7: sixteen lanes read 256 contiguous bytes of a row.
