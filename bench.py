@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import re
 import sys
@@ -368,6 +369,7 @@ def prepare(name: str):
 
 
 SETTLE_S = 0.1  # minimum untimed warm-up, seconds
+CLOCK_SAMPLE_S = 2.5  # the headline's clock and power loop, seconds
 
 
 def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
@@ -425,6 +427,74 @@ def summary(p, sec: float, kname: str) -> dict:
         "roofline_tflops": round(p.rf.attainable / 1e12, 1),
         "frac": round(p.rf.fraction(sec), 4),
     }
+
+
+def stream_probe(nbytes: int, copy: bool = False, steps: int = 100, warmup: int = 50,
+                 grids=(512, 1024, 2048, 4096)) -> dict:
+    """The library's device bandwidth probe (gemm_probe_stream) on `nbytes`:
+    a flat streaming read (or copy) of that many bytes, rotated over enough
+    buffers to exceed the last-level cache like the GEMM operands, event-timed
+    for each grid size; the best is the practical floor for a kernel that
+    reads the same bytes once."""
+    import torch
+    from roofline_driven_optimisation_amd import binding
+    sets = max(1, -(-ROTATE_BYTES // nbytes))
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda")
+            for i in range(sets)]
+    dsts = [torch.empty_like(b) for b in bufs] if copy else None
+    out = torch.empty(max(grids), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(i, g):
+        binding.probe_stream(bufs[i % sets], out=out, dst=dsts[i % sets] if copy else None,
+                             blocks=g, stream=stream)
+
+    per = {}
+    for g in grids:
+        for i in range(warmup):
+            run(i, g)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            run(i, g)
+        end.record(stream)
+        torch.cuda.synchronize()
+        per[g] = start.elapsed_time(end) * 1e3 / steps
+    best = min(per, key=per.get)
+    moved = nbytes * (2 if copy else 1)
+    del bufs, dsts
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "kind": "copy" if copy else "read", "us": round(per[best], 2),
+            "tbs": round(moved / per[best] / 1e6, 3), "blocks": best,
+            "us_by_blocks": {str(g): round(v, 2) for g, v in per.items()}}
+
+
+def lds_bank_probe(strides=(1, 2, 4, 8, 16, 32, 64), steps: int = 4096, blocks: int = 512,
+                   reps: int = 20) -> dict:
+    """The library's shared-memory bank probe (gemm_probe_lds): time per
+    launch, and per 4-byte read of one wave, for lane strides that put 1, 2,
+    4, ... 64 lanes of a wave on one of the 64 banks."""
+    import torch
+    from roofline_driven_optimisation_amd import binding
+    out = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for st in strides:
+        for _ in range(3):
+            binding.probe_lds(st, steps, out, blocks=blocks, stream=stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            binding.probe_lds(st, steps, out, blocks=blocks, stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / reps
+        res[str(st)] = {"us": round(us, 2),
+                        "lanes_per_bank": math.gcd(st, 64)}
+    base = res[str(strides[0])]["us"]
+    for v in res.values():
+        v["slowdown"] = round(v["us"] / base, 2)
+    return {"steps": steps, "blocks": blocks, "by_stride": res}
 
 
 def launch_floor(per_graph: int = 200, replays: int = 10) -> dict:
@@ -510,12 +580,14 @@ def sample_smi():
     return {"gfx0_clock_mhz": float(clk.group(1)), "socket_power_w": float(pw.group(1))}
 
 
-def sustain(name: str, seconds: float) -> dict:
+def sustain(name: str, seconds: float, p=None) -> dict:
     """Launch one workload back to back for `seconds` while amd-smi samples the
-    clock and board power (steady state: power- and thermally-settled)."""
+    clock and board power (steady state: power- and thermally-settled); `p`
+    is the prepared workload, else it is prepared here."""
     import threading
     import torch
-    p = prepare(name)
+    if p is None:
+        p = prepare(name)
     kname = p.kernel_name()
     samples = []
 
@@ -703,6 +775,18 @@ def main():
     kname = head.kernel_name()
     log("bench: timing %s (%s), %d steps" % (HEADLINE, kname, args.steps))
     wall, ev = time_workload(head, args.steps, args.warmup)
+    # the clock and power the headline holds, from a short back-to-back loop
+    # after (not inside) the timed steps
+    held = sustain(HEADLINE, CLOCK_SAMPLE_S, head)
+    smi = held["smi_samples"]
+    clock = {"how": "amd-smi, every 0.5 s of a %.1f s back-to-back loop of the headline "
+                    "after its timed steps" % CLOCK_SAMPLE_S, "us_in_loop": held["us"]}
+    if smi:
+        clock["gfx_clock_mhz"] = [min(x["gfx0_clock_mhz"] for x in smi),
+                                  max(x["gfx0_clock_mhz"] for x in smi)]
+        clock["socket_power_w"] = [min(x["socket_power_w"] for x in smi),
+                                   max(x["socket_power_w"] for x in smi)]
+    log("bench: clock " + json.dumps(clock))
     records = []
     head_rf = head.rf
     if cpu:
@@ -739,6 +823,19 @@ def main():
 
     floor = launch_floor()
     log("bench: launch floor " + json.dumps(floor))
+    # the flat-read floor of the decode GEMMs' weight bytes, and a copy
+    probes = {"read_4096x11008_bf16": stream_probe(4096 * 11008 * 2),
+              "read_4096x32000_bf16": stream_probe(4096 * 32000 * 2),
+              "copy_1GiB": stream_probe(1 << 30, copy=True)}
+    log("bench: bandwidth probes " + json.dumps(probes))
+    lds = lds_bank_probe()
+    log("bench: shared-memory bank probe " + json.dumps(lds))
+    flat = {v["bytes"]: v["us"] for k, v in probes.items() if v["kind"] == "read"}
+    for s_ in also:
+        if s_["bound"] == "hbm" and "K" in s_ and s_["K"] * s_["N"] * 2 in flat:
+            # the same weight bytes read flat: the floor this kernel is held to
+            s_["flat_read_us"] = flat[s_["K"] * s_["N"] * 2]
+            s_["vs_flat_read"] = round(s_["flat_read_us"] / s_["us"], 4)
     for s_ in also:
         if s_["bound"] == "hbm":
             body = s_["us"] - floor["us"]
@@ -773,7 +870,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "also": also,
+        "clock": clock,
         "launch_floor": floor,
+        "bandwidth_probes": probes,
+        "lds_bank_probe": lds,
         "ladder": ladder,
         "page_context": PAGE_CONTEXT,
     }

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define GEMM_ABI_VERSION 7
+#define GEMM_ABI_VERSION 8
 
 #if defined(__GNUC__) || defined(__clang__)
 #define GEMM_API __attribute__((visibility("default")))
@@ -273,6 +273,38 @@ GEMM_API int gemm_bf16_strided_batched(int batch, int M, int N, int K, float alp
  */
 GEMM_API int reduce_sum_f32(const float *x, int64_t n, float *out, void *stream);
 GEMM_API int reduce_sum_f32_naive(const float *x, int64_t n, float *out, void *stream);
+
+/*
+ * Measurement probes: the hands-on exercises that close page "Memory
+ * hierarchy and cost table" (section 4.8), a device-to-device bandwidth test
+ * and a shared-memory bank-conflict demonstration (section 4.3.2).  They
+ * compute nothing of the GEMM; bench.py times them beside it.  Asynchronous
+ * on `stream` like the GEMMs; every pointer is a device pointer owned by
+ * the caller; `blocks` (1 .. 2^20) is the number of 256-thread workgroups.
+ *
+ * gemm_probe_stream reads the `bytes` bytes at src (a multiple of 16,
+ * src 16-byte aligned) once, every 16-byte chunk with one load, the whole
+ * grid streaming one contiguous region at a time.  dst == NULL: out (blocks
+ * words) receives one XOR per workgroup, and the XOR of all of them is the
+ * XOR of every 32-bit word of src.  dst != NULL (16-byte aligned, not
+ * overlapping src): src is copied to dst and out is not used (may be NULL).
+ * Its time is the practical floor of any kernel that reads (or copies) as
+ * many bytes.
+ *
+ * gemm_probe_lds has every lane of each workgroup read `steps` 4-byte words
+ * of a 64 KB shared-memory table whose word i holds i * 2654435761 (mod
+ * 2^32): lane l of wave w reads words l * stride + 17 w + j, j = 0 .. steps
+ * - 1, so `stride` sets how many lanes of a wave share one of the 64 banks
+ * (1: none; 2: pairs; 64: all).  out (blocks words) receives, per
+ * workgroup, the XOR of every word its lanes read.  63 stride + 51 + steps
+ * must not exceed 16384.
+ *
+ * Argument errors (sizes, alignment, NULL where a pointer is needed) return
+ * GEMM_ERR_INVALID_ARG and launch nothing.
+ */
+GEMM_API int gemm_probe_stream(const void *src, void *dst, int64_t bytes, uint32_t *out,
+                               int blocks, void *stream);
+GEMM_API int gemm_probe_lds(int stride, int steps, uint32_t *out, int blocks, void *stream);
 
 /* Static English text for a gemm_status value (never NULL). */
 GEMM_API const char *gemm_status_string(int status);

@@ -79,6 +79,10 @@ def library():
         lib.gemm_split_timeouts.restype = ctypes.c_int
         lib.gemm_test_hook.argtypes = [i, ctypes.c_longlong, vp]
         lib.gemm_test_hook.restype = ctypes.c_int
+        lib.gemm_probe_stream.argtypes = [vp, vp, ctypes.c_int64, vp, i, vp]
+        lib.gemm_probe_stream.restype = ctypes.c_int
+        lib.gemm_probe_lds.argtypes = [i, i, vp, i, vp]
+        lib.gemm_probe_lds.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -305,6 +309,47 @@ def reduce_sum_f32(x, out, stream=None, naive=False):
     if status != GEMM_OK:
         raise GemmError(status, _status_message(status))
     return out
+
+
+def probe_stream(src, out=None, dst=None, blocks=2048, stream=None):
+    """The device bandwidth probe (gemm_probe_stream): read every byte of the
+    GPU tensor src once, XOR-folding it into out (uint32 or int32, `blocks`
+    words), or copy it into dst when dst is given.  src (and dst) must be
+    contiguous, 16-byte aligned, a multiple of 16 bytes long."""
+    import torch
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst is not None:
+        if (not isinstance(dst, torch.Tensor) or dst.device != src.device or
+                not dst.is_contiguous() or dst.numel() * dst.element_size() < nbytes):
+            raise ValueError("dst must be a contiguous GPU tensor on src's device, as large")
+    if dst is None and (out is None or out.device != src.device or out.element_size() != 4 or
+                        not out.is_contiguous() or out.numel() < blocks):
+        raise ValueError("out must hold `blocks` 32-bit words on src's device")
+    with torch.cuda.device(src.device):
+        status = library().gemm_probe_stream(
+            ctypes.c_void_p(src.data_ptr()),
+            ctypes.c_void_p(dst.data_ptr() if dst is not None else 0), nbytes,
+            ctypes.c_void_p(out.data_ptr() if out is not None else 0), int(blocks),
+            _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
+
+
+def probe_lds(stride, steps, out, blocks=512, stream=None):
+    """The shared-memory bank probe (gemm_probe_lds): `steps` 4-byte reads
+    per lane at lane stride `stride`; out (32-bit words on the GPU, at least
+    `blocks`) receives each workgroup's XOR of what it read."""
+    import torch
+    if out.device.type != "cuda" or out.element_size() != 4 or not out.is_contiguous() or \
+            out.numel() < blocks:
+        raise ValueError("out must hold `blocks` 32-bit words on the GPU")
+    with torch.cuda.device(out.device):
+        status = library().gemm_probe_lds(int(stride), int(steps), ctypes.c_void_p(out.data_ptr()),
+                                          int(blocks), _stream_handle(stream))
+    if status != GEMM_OK:
+        raise GemmError(status, _status_message(status))
 
 
 def gemm(A, B, C, alpha=1.0, beta=0.0, stream=None):

@@ -190,6 +190,21 @@ hipError_t launch_reduce_sum(const float *x, long long n, float *out, float *par
 hipError_t launch_reduce_sum_tree(const float *x, long long n, float *out, float *scratch,
                                   long long scratch_floats, hipStream_t stream);
 
+// Measurement probes (probes.hip).  launch_stream_probe reads `bytes`
+// (a multiple of 16; src 16-byte aligned) with `blocks` workgroups of 256
+// threads: dst == nullptr XORs the words and writes workgroup b's XOR to
+// out[b] (`blocks` words); otherwise it copies src to dst (out unused).
+// launch_lds_probe runs `steps` 4-byte LDS reads per lane at word
+// lane * stride + step + 17 wave (63 stride + 51 + steps must not exceed
+// kLdsProbeWords, else hipErrorInvalidValue) of a table holding
+// word i = i * 2654435761 (mod 2^32), and writes workgroup b's XOR of
+// what its lanes read to out[b].
+constexpr int kLdsProbeWords = 16384;  // 64 KB of LDS
+hipError_t launch_stream_probe(const void *src, void *dst, long long bytes, uint32_t *out,
+                               int blocks, hipStream_t stream);
+hipError_t launch_lds_probe(int stride, int steps, uint32_t *out, int blocks,
+                            hipStream_t stream);
+
 // Runs a probe grid on `stream`, waits for it, and sets *ok when every
 // workgroups whose ids are equal modulo kXcdCount ran on one XCD and the
 // kXcdCount residues on different XCDs (which XCD takes workgroup 0 varies

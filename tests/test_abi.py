@@ -34,7 +34,7 @@ def test_header_declares_expected_api():
     for n in ("gemm_f32", "gemm_bf16", "gemm_naive_f32", "gemm_naive_bf16",
               "gemm_f32_bias_act", "gemm_bf16_bias_act", "reduce_sum_f32", "reduce_sum_f32_naive",
               "gemm_bf16_strided_batched", "gemm_fp8", "gemm_kernel_name",
-              "gemm_split_timeouts", "gemm_test_hook",
+              "gemm_split_timeouts", "gemm_test_hook", "gemm_probe_stream", "gemm_probe_lds",
               "gemm_status_string", "gemm_last_kernel", "gemm_abi_version"):
         assert n in names
 
@@ -107,3 +107,24 @@ def test_kernel_name_without_gpu(lib):
 def test_diagnostics_argument_errors(lib):
     assert lib.gemm_split_timeouts(None, None) == 1
     assert lib.gemm_test_hook(99, 0, None) == 1
+
+
+def test_probe_argument_errors(lib):
+    """The probes' argument checks return before any HIP call."""
+    p = ctypes.c_void_p(256)  # never dereferenced
+    u = ctypes.c_void_p(260)  # not 16-byte aligned
+    assert lib.gemm_probe_stream(p, None, -16, p, 1, None) == 1        # negative size
+    assert lib.gemm_probe_stream(p, None, 24, p, 1, None) == 1         # not a multiple of 16
+    assert lib.gemm_probe_stream(u, None, 32, p, 1, None) == 1         # misaligned src
+    assert lib.gemm_probe_stream(p, u, 32, None, 1, None) == 1         # misaligned dst
+    assert lib.gemm_probe_stream(None, None, 32, p, 1, None) == 1      # no src
+    assert lib.gemm_probe_stream(p, None, 32, None, 1, None) == 1      # read with no out
+    assert lib.gemm_probe_stream(p, None, 32, p, 0, None) == 1         # no workgroups
+    assert lib.gemm_probe_stream(p, None, 32, p, (1 << 20) + 1, None) == 1
+    assert lib.gemm_probe_lds(1, 8, None, 1, None) == 1                # no out
+    assert lib.gemm_probe_lds(-1, 8, p, 1, None) == 1
+    assert lib.gemm_probe_lds(1, -1, p, 1, None) == 1
+    assert lib.gemm_probe_lds(1, 8, p, 0, None) == 1
+    assert lib.gemm_probe_lds(64, 16384 - 63 * 64 - 51 + 1, p, 1, None) == 1  # past the table
+    assert lib.gemm_probe_lds(300, 8, p, 1, None) == 1               # lanes past the table
+    assert lib.gemm_last_kernel() == b"none"
