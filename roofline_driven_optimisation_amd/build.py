@@ -34,8 +34,8 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC] + CFLAGS + list(extra) + ["-c", src, "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
@@ -43,27 +43,32 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every kernel source and link libgemm.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra=(), lib: str = LIB, build_dir: str = BUILD_DIR,
+          check_load: bool = True) -> str:
+    """Compile every kernel source and link libgemm.so; returns its path.
+    ``extra`` flags go to every compile and the link; ``lib`` and
+    ``build_dir`` place a variant build elsewhere (a host-sanitizer build,
+    which loads only with its runtime preloaded: ``check_load=False``)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + list(extra) + ["-o", tmp] + objs
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (proc.stdout, proc.stderr))
     # a kernel whose host stub was not emitted only shows up at load time
-    try:
-        ctypes.CDLL(tmp)
-    except OSError as exc:
-        os.unlink(tmp)
-        raise RuntimeError("built library does not load: %s" % exc)
-    os.replace(tmp, LIB)
+    if check_load:
+        try:
+            ctypes.CDLL(tmp)
+        except OSError as exc:
+            os.unlink(tmp)
+            raise RuntimeError("built library does not load: %s" % exc)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
