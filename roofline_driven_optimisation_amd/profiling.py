@@ -170,6 +170,87 @@ def mfma_rows(path: str, last: int = 0):
     return rows
 
 
+def counter_runs(paths, labels, last: int = 8, kernels=("bf16_q4", "fp8_q4")):
+    """Median counter values per workload from one or more --pmc passes of
+    the same bench command: each pass's dispatches are split into runs of
+    consecutive dispatches of one kernel and launch shape (one run per
+    workload, as in dispatch_stats), runs of the named kernel families with
+    at least 5 dispatches are matched in order to ``labels``, and every
+    counter is the median over the last ``last`` dispatches of its run
+    (summed over the device).  Returns {label: {counter: value, "us": ...}}."""
+    out = {}
+    for path in paths:
+        with open(path) as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+        disp, order = {}, []
+        for r in rows:
+            d = r.get("Dispatch_Id") or r["Start_Timestamp"]
+            if d not in disp:
+                wg = max(int(r.get("Workgroup_Size", 1) or 1), 1)
+                disp[d] = {"key": (short_name(r["Kernel_Name"]),
+                                   int(r.get("Grid_Size", 0) or 0) // wg),
+                           "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3}
+                order.append(d)
+            disp[d][r["Counter_Name"]] = disp[d].get(r["Counter_Name"], 0.0) + float(
+                r["Counter_Value"])
+        runs = []
+        for d in order:
+            k = disp[d]["key"]
+            if runs and runs[-1][0] == k:
+                runs[-1][1].append(disp[d])
+            else:
+                runs.append((k, [disp[d]]))
+        runs = [v for k, v in runs if len(v) >= 5 and k[0].startswith(tuple(kernels))]
+        for label, v in zip(labels, runs):
+            tail = v[-last:]
+            got = out.setdefault(label, {})
+            for c in tail[0]:
+                if c != "key":
+                    got[c] = statistics.median(x[c] for x in tail if c in x)
+    return out
+
+
+def account_markdown(runs) -> str:
+    """Where a wave's cycles go, from counter_runs over the passes: the SQ
+    wave-cycle counters partition a wave's life into issuing (ACTIVE_INST_ANY),
+    waiting to issue (WAIT_INST_ANY: a dependency or a busy unit, the matrix
+    core included) and waiting on anything else (WAIT_ANY: s_waitcnt,
+    barriers); the issuing share is split by instruction type."""
+    out = ["| counter | " + " | ".join(runs) + " |", "|---|" + "---|" * len(runs)]
+    rows = [("dispatch us (under counters)", lambda c: "%.1f" % c["us"])]
+    for name, num in (("issuing (ACTIVE_INST_ANY)", "SQ_ACTIVE_INST_ANY"),
+                      ("waiting to issue (WAIT_INST_ANY)", "SQ_WAIT_INST_ANY"),
+                      ("waiting on s_waitcnt / barrier (WAIT_ANY)", "SQ_WAIT_ANY"),
+                      ("  issuing scalar (ACTIVE_INST_SCA)", "SQ_ACTIVE_INST_SCA"),
+                      ("  issuing vector ALU incl. MFMA (ACTIVE_INST_VALU)", "SQ_ACTIVE_INST_VALU"),
+                      ("  issuing LDS (ACTIVE_INST_LDS)", "SQ_ACTIVE_INST_LDS"),
+                      ("  issuing vector memory (ACTIVE_INST_VMEM)", "SQ_ACTIVE_INST_VMEM")):
+        rows.append((name + ", % of wave cycles",
+                     lambda c, n=num: "%.1f" % (100 * c[n] / c["SQ_WAVE_CYCLES"])))
+    rows += [("MFMA busy cycles per SIMD", lambda c: "%.0f" % (c["SQ_VALU_MFMA_BUSY_CYCLES"] / NUM_SIMD)),
+             ("cycles per wave (4 x SQ_WAVE_CYCLES / waves)",
+              lambda c: "%.0f" % (4 * c["SQ_WAVE_CYCLES"] / c["SQ_WAVES"])),
+             ("vector-memory latency, cycles (VmemLatency)", lambda c: "%.0f" % c["VmemLatency"]),
+             ("LDS latency, cycles (LdsLatency)", lambda c: "%.0f" % c["LdsLatency"]),
+             ("TA address FIFO full, cycles per CU", lambda c: "%.0f" % (c["SQ_VMEM_TA_ADDR_FIFO_FULL"] / 256)),
+             ("TA command FIFO full, cycles per CU", lambda c: "%.0f" % (c["SQ_VMEM_TA_CMD_FIFO_FULL"] / 256)),
+             ("LDS data FIFO full, cycles per CU", lambda c: "%.0f" % (c["SQ_LDS_DATA_FIFO_FULL"] / 256)),
+             ("scalar instructions per wave", lambda c: "%.0f" % (c["SQ_INSTS_SALU"] / c["SQ_WAVES"])),
+             ("vector ALU instructions per wave (MFMA included)", lambda c: "%.0f" % (c["SQ_INSTS_VALU"] / c["SQ_WAVES"])),
+             ("MFMA instructions per wave", lambda c: "%.0f" % (c["SQ_INSTS_MFMA"] / c["SQ_WAVES"])),
+             ("LDS instructions per wave", lambda c: "%.0f" % (c["SQ_INSTS_LDS"] / c["SQ_WAVES"])),
+             ("vector-memory instructions per wave", lambda c: "%.0f" % (c["SQ_INSTS_VMEM"] / c["SQ_WAVES"]))]
+    for name, fn in rows:
+        cells = []
+        for c in runs.values():
+            try:
+                cells.append(fn(c))
+            except (KeyError, ZeroDivisionError):
+                cells.append("-")
+        out.append("| %s | %s |" % (name, " | ".join(cells)))
+    return "\n".join(out)
+
+
 def mfma_markdown(rows) -> str:
     out = ["| kernel | us (under counters) | MFMA GFLOP counted | MFMA busy cycles per SIMD | "
            "wave cycles waiting (any) | wave cycles waiting (LDS) |",
@@ -213,6 +294,11 @@ def main():
                        "SQ_WAIT_INST_ANY, SQ_WAIT_INST_LDS")
     m.add_argument("dir")
     m.add_argument("--last", type=int, default=0)
+    a = sub.add_parser("account", help="where a wave's cycles go, from several --pmc passes "
+                       "of the same bench command (one run per workload)")
+    a.add_argument("dirs", nargs="+")
+    a.add_argument("--labels", required=True, help="comma-separated workload names, in order")
+    a.add_argument("--last", type=int, default=8)
     c = sub.add_parser("counters", help="calibrated HBM bytes per dispatch")
     c.add_argument("--fetch", required=True, help="dir of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="dir of the WRITE_SIZE run")
@@ -225,6 +311,11 @@ def main():
         return
     if args.cmd == "mfma":
         print(mfma_markdown(mfma_rows(_find(args.dir, "_counter_collection.csv"), args.last)))
+        return
+    if args.cmd == "account":
+        runs = counter_runs([_find(d, "_counter_collection.csv") for d in args.dirs],
+                            args.labels.split(","), args.last)
+        print(account_markdown(runs))
         return
     if args.cmd == "trace":
         print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"), args.last)))

@@ -57,3 +57,30 @@ def test_dispatch_stats_splits_runs_of_one_kernel(tmp_path):
     assert [r["calls"] for r in steady] == [5, 5]
     assert [r["avg_us"] for r in steady] == [4.0, 8.0]
     assert steady[0]["kernel"] == steady[1]["kernel"] == "gemm_kernel<true> [256 workgroups x 256]"
+
+
+def test_counter_runs_label_consecutive_runs(tmp_path):
+    """Counter passes: two workloads on the same kernel and grid, with
+    another kernel between them, get their own medians, matched to the
+    labels in time order; short runs (warm-up copies) are skipped."""
+    import csv
+    from roofline_driven_optimisation_amd.profiling import counter_runs
+    path = tmp_path / "p_counter_collection.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Start_Timestamp",
+                    "End_Timestamp", "Counter_Name", "Counter_Value"])
+        t, d = 0, 0
+        for kernel, grid, value, n in (("bf16_q4_kernel<false>", 65536, 10.0, 6),
+                                       ("fp8_q4_kernel<false, 0>", 65536, 20.0, 6),
+                                       ("bf16_q4_kernel<false>", 65536, 30.0, 6),
+                                       ("bf16_q4_kernel<false>", 1024, 99.0, 2)):
+            for i in range(n):
+                d += 1
+                for se in range(2):  # per-SE rows are summed
+                    w.writerow([d, kernel, grid, 256, t, t + 5000, "SQ_WAVES", value / 2])
+                t += 10000
+    runs = counter_runs([str(path)], ["a", "b", "c"], last=4)
+    assert list(runs) == ["a", "b", "c"]
+    assert [runs[k]["SQ_WAVES"] for k in "abc"] == [10.0, 20.0, 30.0]
+    assert runs["a"]["us"] == 5.0
