@@ -235,6 +235,22 @@ def test_fp8_full_size(shape, fmt):
     assert err <= fp8_tol(K, name)
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
+@pytest.mark.parametrize("shape", FULL, ids=lambda c: "%dx%dx%d" % c[:3])
+def test_fp8_full_size_integers(shape, fmt):
+    """The benchmarked sizes with integer entries in [-4, 4] (exact in both
+    formats; every product, group sum and partial sum is an integer below
+    2^24, so exact in fp32 whatever the summation): the whole output must
+    equal the product of the oracle's decoded operands, element for
+    element, split tiles included."""
+    M, N, K, want = shape
+    A, B, _ = draw(M, N, K, fmt, "int", seed=8)
+    got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
+    assert name == want, name
+    ref = oracle.fp8_decode(A, fmt) @ oracle.fp8_decode(B, fmt).T
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
 def test_fp8_bad_arguments():
     import torch
     lib = binding.library()

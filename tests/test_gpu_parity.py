@@ -114,7 +114,9 @@ def test_workload_full(name):
 
 @pytest.mark.parametrize("name", ["f32_4092", "f32_4096", "bf16_4096", "prefill_qkv",
                                   "prefill_o", "prefill_down", "prefill_gate_up",
-                                  "decode_down_m16", "decode_lm_head"])
+                                  "decode_up_m1", "decode_up_m8", "decode_up_m16",
+                                  "decode_down_m1", "decode_down_m8", "decode_down_m16",
+                                  "decode_lm_head"])
 def test_workload_integer_exact(name):
     """Full-size shapes with integer entries in [-2, 2]: the exact product is
     known in fp64 for every element, so the whole output must match it."""
