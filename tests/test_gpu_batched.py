@@ -18,6 +18,11 @@ from roofline_driven_optimisation_amd.inputs import f32_to_bf16_bits
 pytestmark = pytest.mark.gpu
 
 
+def widen(bits):
+    """bf16 bit patterns to their exact values (the upper half of an fp32)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def draw(shape, dist, rng):
     if dist.startswith("i:"):
         r = int(dist[2:])
@@ -100,6 +105,25 @@ def test_attention_shapes_full(trans_b):
         worst = max(worst, oracle.parity_error(got[h], ref, den))
     log("  attention %s, all %d heads, err=%.3e" % ("qk" if trans_b else "pv", H, worst))
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("trans_b", [True, False], ids=["qk", "pv"])
+def test_attention_shapes_integers(trans_b):
+    """The same 32-head shapes with integer entries in [-3, 3]: every partial
+    sum is an integer below 2^24, so all 32 heads' outputs must equal the
+    exact products bit for bit."""
+    H, T, d = 32, 2048, 128
+    M, N, K = (T, T, d) if trans_b else (T, d, T)
+    rng = np.random.default_rng(4)
+    A = f32_to_bf16_bits(rng.integers(-3, 4, (H, M, K)).astype(np.float32))
+    Bs = (H, N, K) if trans_b else (H, K, N)
+    B = f32_to_bf16_bits(rng.integers(-3, 4, Bs).astype(np.float32))
+    got, name = run(A, B, None, 1.0, 0.0, trans_b, N)
+    assert name.startswith("bf16_"), name
+    a = widen(A)
+    b = widen(B)
+    ref = a @ (np.swapaxes(b, 1, 2) if trans_b else b)
+    assert np.array_equal(got.astype(np.float64), ref)
 
 
 def test_shared_operand_stride_zero():

@@ -142,6 +142,22 @@ def test_bias_only_and_activation_only(monkeypatch):
     check(case, got, None, binding.ACT_GELU)
 
 
+@pytest.mark.parametrize("name,act", [("prefill_gate_up", binding.ACT_GELU),
+                                      ("decode_up_m1", binding.ACT_SILU)],
+                         ids=["prefill_gate_up+bias_gelu", "decode_up_m1+bias_silu"])
+def test_benchmarked_fused_workloads_full(name, act):
+    """The two fused workloads the benchmark times, at full size with its
+    inputs (the workload's operands, a normal(0, 0.5) bias, seed 0), every
+    element against the oracle's epilogue."""
+    from roofline_driven_optimisation_amd.inputs import workload
+    w = workload(name)
+    case = w.case(0)
+    bias = make_bias(w.N, "n:0.5", 0)
+    got, kname = run_epi(case, bias, act)
+    log("  kernel %s" % kname)
+    check(case, got, bias, act)
+
+
 def test_bad_activation_rejected():
     import torch
     case = make_case(8, 8, 8, "bf16", seed=1)
