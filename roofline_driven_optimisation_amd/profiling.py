@@ -200,12 +200,15 @@ def counter_runs(paths, labels, last: int = 8, kernels=("bf16_q4", "fp8_q4")):
                 runs[-1][1].append(disp[d])
             else:
                 runs.append((k, [disp[d]]))
-        runs = [v for k, v in runs if len(v) >= 5 and k[0].startswith(tuple(kernels))]
-        for label, v in zip(labels, runs):
+        runs = [(k, v) for k, v in runs if len(v) >= 5 and
+                (k[0].startswith(tuple(kernels)) if kernels else not k[0].startswith("__amd"))]
+        for label, (k, v) in zip(labels, runs):
+            out.setdefault(label, {})["kernel"] = "%s [%d workgroups]" % k
+        for label, (k, v) in zip(labels, runs):
             tail = v[-last:]
             got = out.setdefault(label, {})
             for c in tail[0]:
-                if c != "key":
+                if c not in ("key", "kernel"):
                     got[c] = statistics.median(x[c] for x in tail if c in x)
     return out
 
@@ -305,6 +308,8 @@ def main():
     c.add_argument("--copy-fetch", required=True, help="dir of the copy probe's FETCH_SIZE run")
     c.add_argument("--copy-write", required=True, help="dir of the copy probe's WRITE_SIZE run")
     c.add_argument("--copy-mib", type=float, required=True)
+    c.add_argument("--labels", default="", help="comma-separated workload names, in the order "
+                   "the bench ran them: one row per workload run instead of per kernel")
     args = ap.parse_args()
     if args.cmd == "stats":
         print(stats_markdown(kernel_stats(_find(args.dir, "_kernel_stats.csv"))))
@@ -329,6 +334,20 @@ def main():
     w_fac = kib / max(v for (k, n), v in cw.items() if n == "WRITE_SIZE")
     print("calibration: copy of %.0f MiB -> FETCH_SIZE factor %.3f, WRITE_SIZE factor %.3f"
           % (args.copy_mib, f_fac, w_fac))
+    if args.labels:
+        labels = args.labels.split(",")
+        fr = counter_runs([_find(args.fetch, "_counter_collection.csv")], labels, 8, None)
+        wr = counter_runs([_find(args.write, "_counter_collection.csv")], labels, 8, None)
+        for lab in labels:
+            if lab not in fr or lab not in wr:
+                continue
+            fb = fr[lab]["FETCH_SIZE"] * 1024 * f_fac
+            wb = wr[lab]["WRITE_SIZE"] * 1024 * w_fac
+            kern = fr[lab].get("kernel", "")
+            print("%s, %s: fetch %.1f MB, write %.1f MB, total %.1f MB per dispatch (source %s)"
+                  % (lab, kern, fb / 1e6, wb / 1e6, (fb + wb) / 1e6,
+                     source_hash(kern.split("<")[0])))
+        return
     for (k, n), v in sorted(fetch.items()):
         w = write.get((k, "WRITE_SIZE"), float("nan"))
         fb, wb = v * 1024 * f_fac, w * 1024 * w_fac
