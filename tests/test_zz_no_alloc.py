@@ -8,6 +8,8 @@ ABI against gemm_bf16 on the same seeded inputs.
 * A large-M call runs whole tiles and matches gemm_bf16.
 * A decode-shaped call that needs more scratch than the array holds is
   refused with GEMM_ERR_SCRATCH and leaves C untouched.
+* Under graph capture (on a stream with no workspace) the decode call still
+  splits K through the static array, and every replay is exact.
 * In a fresh child process (where the first call sets the array up and
   runs the XCD probe itself): once every shape has run, further calls of
   all of them leave the device's free memory unchanged.
@@ -99,6 +101,38 @@ def test_noalloc_refuses_oversized():
     assert rc == GEMM_ERR_SCRATCH and k == "none", (rc, k)
     assert np.all(C == 7.0)
     assert binding.library().gemm_status_string(rc).decode().startswith("the call needs more")
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for include code under HIP graph capture: after one
+    direct call has set the array up, a decode-shaped call captured on a
+    fresh stream (which has no workspace of its own) splits K through the
+    static array, and four replays, with eager calls of both entry points
+    on another shape between them, each give the oracle's result exactly
+    (the kernel re-arms its counters, so every replay starts clean)."""
+    import torch
+    case = make_case(16, 4096, 2048, "bf16", 1.5, 0.5, "i:4", "i:4", "i:4", seed=65)
+    ref, _ = oracle.gemm(case.A, case.B, case.C, 1.5, 0.5, bf16=True)
+    A, B, C = to_device(case)
+    C0 = C.clone()
+    rc, k, _ = call("gemm_bf16_noalloc", case)  # set-up on this device (if not done yet)
+    assert rc == 0 and k == "skinny_bf16_splitk_xcd_static", (rc, k)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.gemm_bf16_noalloc(A, B, C, 1.5, 0.5)
+    assert binding.last_kernel() == "skinny_bf16_splitk_xcd_static", binding.last_kernel()
+    other = make_case(8, 1024, 512, "bf16", 1.0, 0.0, "i:4", "i:4", seed=66)
+    oA, oB, oC = to_device(other)
+    for r in range(4):
+        C.copy_(C0)
+        g.replay()
+        torch.cuda.synchronize()
+        log("  graph replay %d" % r)
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), r
+        binding.gemm_bf16_noalloc(oA, oB, oC, 1.0, 0.0)
+        binding.gemm_bf16(oA, oB, oC, 1.0, 0.0)
+        torch.cuda.synchronize()
 
 
 def test_noalloc_fresh_process_allocates_nothing():
