@@ -726,6 +726,9 @@ def main():
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                     help="only launch the --only workloads (default: the headline) back to "
                     "back for SECONDS each, sampling clock and power with amd-smi")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the library's bandwidth and LDS bank probes (one JSON line "
+                    "each; for profiling them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times "
                     "(calibrates the HBM byte counters)")
@@ -754,6 +757,12 @@ def main():
         sec = (time.perf_counter() - t0) / args.steps
         log(json.dumps({"copy_mib": args.copy_probe, "us": round(sec * 1e6, 2),
                         "gbs_read_plus_write": round(2 * n / sec / 1e9, 1)}))
+        return
+
+    if args.probes:
+        log(json.dumps({"read_4096x11008_bf16": stream_probe(4096 * 11008 * 2, steps=args.steps,
+                                                             warmup=args.warmup)}))
+        log(json.dumps({"lds_bank_probe": lds_bank_probe(reps=args.steps)}))
         return
 
     if args.sustain > 0:

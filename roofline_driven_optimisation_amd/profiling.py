@@ -254,6 +254,36 @@ def account_markdown(runs) -> str:
     return "\n".join(out)
 
 
+def lds_probe_rows(path: str, strides, skip: int = 3):
+    """Bank-conflict counters of the LDS probe (bench.py --probes): its
+    dispatches come in one group per stride, in order, `skip` warm-up
+    launches first; per stride, the medians over the rest of SQ_INSTS_LDS,
+    SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT, and the extra LDS cycles
+    per conflict-free one, conflict / (active - conflict)."""
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    disp, order = {}, []
+    for r in rows:
+        if not short_name(r["Kernel_Name"]).startswith("lds_probe"):
+            continue
+        d = r.get("Dispatch_Id") or r["Start_Timestamp"]
+        if d not in disp:
+            disp[d] = {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3}
+            order.append(d)
+        disp[d][r["Counter_Name"]] = disp[d].get(r["Counter_Name"], 0.0) + float(
+            r["Counter_Value"])
+    per = len(order) // max(len(strides), 1)
+    out = []
+    for i, st in enumerate(strides):
+        group = [disp[d] for d in order[i * per:(i + 1) * per]][skip:]
+        med = {k: statistics.median(x[k] for x in group if k in x) for k in group[0]}
+        act, conf = med.get("SQ_LDS_IDX_ACTIVE", 0.0), med.get("SQ_LDS_BANK_CONFLICT", 0.0)
+        med["stride"] = st
+        med["extra_per_cycle"] = conf / (act - conf) if act > conf else float("nan")
+        out.append(med)
+    return out
+
+
 def mfma_markdown(rows) -> str:
     out = ["| kernel | us (under counters) | MFMA GFLOP counted | MFMA busy cycles per SIMD | "
            "wave cycles waiting (any) | wave cycles waiting (LDS) |",
@@ -302,6 +332,10 @@ def main():
     a.add_argument("dirs", nargs="+")
     a.add_argument("--labels", required=True, help="comma-separated workload names, in order")
     a.add_argument("--last", type=int, default=8)
+    lp = sub.add_parser("lds-probe", help="bank-conflict counters of the LDS probe per stride")
+    lp.add_argument("dir")
+    lp.add_argument("--strides", default="1,2,4,8,16,32,64")
+    lp.add_argument("--skip", type=int, default=3)
     c = sub.add_parser("counters", help="calibrated HBM bytes per dispatch")
     c.add_argument("--fetch", required=True, help="dir of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="dir of the WRITE_SIZE run")
@@ -316,6 +350,19 @@ def main():
         return
     if args.cmd == "mfma":
         print(mfma_markdown(mfma_rows(_find(args.dir, "_counter_collection.csv"), args.last)))
+        return
+    if args.cmd == "lds-probe":
+        rows = lds_probe_rows(_find(args.dir, "_counter_collection.csv"),
+                              [int(x) for x in args.strides.split(",")], args.skip)
+        print("| lanes of a wave on one bank (stride) | us per launch (under counters) | "
+              "LDS instructions | LDS busy cycles | bank-conflict cycles | "
+              "extra cycles per conflict-free cycle |")
+        print("|---|---|---|---|---|---|")
+        for r in rows:
+            print("| %d | %.1f | %.3g | %.4g | %.4g | %.2f |" % (
+                r["stride"], r["us"], r.get("SQ_INSTS_LDS", float("nan")),
+                r.get("SQ_LDS_IDX_ACTIVE", float("nan")), r.get("SQ_LDS_BANK_CONFLICT", float("nan")),
+                r["extra_per_cycle"]))
         return
     if args.cmd == "account":
         runs = counter_runs([_find(d, "_counter_collection.csv") for d in args.dirs],

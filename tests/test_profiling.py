@@ -84,3 +84,29 @@ def test_counter_runs_label_consecutive_runs(tmp_path):
     assert list(runs) == ["a", "b", "c"]
     assert [runs[k]["SQ_WAVES"] for k in "abc"] == [10.0, 20.0, 30.0]
     assert runs["a"]["us"] == 5.0
+
+
+def test_lds_probe_rows_groups_by_stride(tmp_path):
+    """The LDS probe's dispatches are one group per stride (warm-up first);
+    the extra cycles per conflict-free one are conflict / (active - conflict)."""
+    import csv
+    from roofline_driven_optimisation_amd.profiling import lds_probe_rows
+    path = tmp_path / "p_counter_collection.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp",
+                    "Counter_Name", "Counter_Value"])
+        d, t = 0, 0
+        for st in (1, 2, 4):
+            for i in range(5):  # 2 warm-up + 3 timed
+                d += 1
+                conflict = 0 if i < 2 else 100 * (st - 1)
+                w.writerow([d, "lds_probe_kernel(int, int, unsigned int*)", t, t + 1000 * st,
+                            "SQ_LDS_IDX_ACTIVE", 100 * st])
+                w.writerow([d, "lds_probe_kernel(int, int, unsigned int*)", t, t + 1000 * st,
+                            "SQ_LDS_BANK_CONFLICT", conflict])
+                t += 10000
+    rows = lds_probe_rows(str(path), [1, 2, 4], skip=2)
+    assert [r["stride"] for r in rows] == [1, 2, 4]
+    assert [r["extra_per_cycle"] for r in rows] == [0.0, 1.0, 3.0]
+    assert [r["us"] for r in rows] == [1.0, 2.0, 4.0]
