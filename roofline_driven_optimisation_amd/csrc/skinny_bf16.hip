@@ -378,13 +378,19 @@ int skinny_pick_splits(int M, int N, int K, int num_cus, bool xcd_local) {
     //   * through uncached memory at M > 8, where the partials are 16x
     //     larger, the fewest splits that reach every CU, rounded up to a power
     //     of two, win (22.6 us with two splits against 24.0 us with eight at
-    //     16 x 4096 x 11008).
+    //     16 x 4096 x 11008);
+    //   * at M <= 2 with few column blocks, sixteen XCD-local splits, when
+    //     that is at most two workgroups per CU (1 x 11008 x 4096: 32 blocks,
+    //     19.0 us against 19.4 us with eight; at M = 8 or 16 eight stay
+    //     faster, their partials being larger).
     const int col_blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
     const int kblks = (K + kKBlock - 1) / kKBlock;
     const int need = (num_cus + col_blocks - 1) / col_blocks;
     int splits;
     if (10 * col_blocks >= 9 * num_cus) {
         splits = 1;
+    } else if (xcd_local && M <= 2 && 16 * col_blocks <= 2 * num_cus) {
+        splits = 16;
     } else if (M <= 8 || xcd_local) {
         splits = max(8, need);
     } else {
