@@ -369,7 +369,30 @@ def prepare(name: str):
 
 
 SETTLE_S = 0.1  # minimum untimed warm-up, seconds
-CLOCK_SAMPLE_S = 2.5  # the headline's clock and power loop, seconds
+CLOCK_SAMPLE_S = 3.0  # the headline's clock and power loop, seconds
+
+
+_MARKER = []
+
+
+def phase_marker(closing: bool = False):
+    """One launch of the library's smallest kernel, a K = 0 GEMM (C = 0 * C),
+    outside any timed region: on a 1 x 8 C (one workgroup) just before a
+    timed loop, on a 1 x 512 C (two workgroups) just after it.  In a kernel
+    trace the pair encloses exactly a workload's timed launches, which
+    would otherwise run together with its warm-up and what follows.  main()
+    makes the first calls at start-up: a first call allocates and sets up,
+    and such a pause between a warm-up and its timed loop lets the clock
+    move."""
+    import torch
+    from roofline_driven_optimisation_amd import binding
+    if not _MARKER:
+        _MARKER.extend([torch.zeros(1, 0, dtype=torch.bfloat16, device="cuda"),
+                        torch.zeros(0, 512, dtype=torch.bfloat16, device="cuda"),
+                        torch.zeros(1, 512, dtype=torch.float32, device="cuda")])
+    A, B, C = _MARKER
+    n = 512 if closing else 8
+    binding.gemm(A, B[:, :n], C[:, :n], 1.0, 0.0)
 
 
 def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
@@ -388,6 +411,7 @@ def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
         i += 1
         if i % 64 == 0:
             torch.cuda.synchronize()
+    phase_marker()  # outside the timed region: it ends the warm-up in a trace
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -398,6 +422,8 @@ def time_workload(p: Prepared, steps: int, warmup: int, naive: bool = False):
     end.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    phase_marker(closing=True)  # after the timed region: it ends the timed launches in a trace
+    torch.cuda.synchronize()
     event = start.elapsed_time(end) * 1e-3 / steps
     return wall, event
 
@@ -742,6 +768,12 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    # the phase marker's tensors and the library's first K = 0 call, made
+    # here so that no first-use pause falls between a warm-up and its timed
+    # launches
+    phase_marker()
+    phase_marker(closing=True)
+    torch.cuda.synchronize()
 
     if args.copy_probe:
         n = args.copy_probe << 20
@@ -791,10 +823,12 @@ def main():
     clock = {"how": "amd-smi, every 0.5 s of a %.1f s back-to-back loop of the headline "
                     "after its timed steps" % CLOCK_SAMPLE_S, "us_in_loop": held["us"]}
     if smi:
-        clock["gfx_clock_mhz"] = [min(x["gfx0_clock_mhz"] for x in smi),
-                                  max(x["gfx0_clock_mhz"] for x in smi)]
-        clock["socket_power_w"] = [min(x["socket_power_w"] for x in smi),
-                                   max(x["socket_power_w"] for x in smi)]
+        # median over the samples, and their range (a sample can fall on a
+        # moment between the loop's batches)
+        for key, out in (("gfx0_clock_mhz", "gfx_clock_mhz"), ("socket_power_w", "socket_power_w")):
+            vals = sorted(x[key] for x in smi)
+            clock[out] = vals[len(vals) // 2]
+            clock[out + "_range"] = [vals[0], vals[-1]]
     log("bench: clock " + json.dumps(clock))
     records = []
     head_rf = head.rf

@@ -87,24 +87,49 @@ def kernel_stats(path: str):
     return rows
 
 
-def dispatch_stats(path: str, last: int = 0):
+# bench.py's phase markers: K = 0 GEMMs, one workgroup just before a timed
+# loop and two just after it
+MARKER_KERNEL = "scale_kernel"
+
+
+def _marker_index(runs, i, workgroups):
+    return (0 <= i < len(runs) and runs[i][0][0].startswith(MARKER_KERNEL) and
+            runs[i][0][1] == workgroups)
+
+
+def dispatch_stats(path: str, last: int = 0, gap_ms: float = 0.0, timed: bool = False):
     """Statistics from a ``*_kernel_trace.csv``, one row per run of
     consecutive dispatches of one kernel with one launch shape (a benchmark
     times its workloads one after another, so two workloads that launch the
     same kernel on the same grid still come out as separate rows, in time
     order).  With ``last`` > 0 only runs of at least ``last`` dispatches are
     reported, each by its last ``last`` dispatches: the timed, steady-state
-    launches of each workload, not the warm-up or the copies between them."""
+    launches of each workload, not the warm-up or the copies between them.
+    With ``gap_ms`` > 0 a run also ends where the device sat idle longer
+    than that between two dispatches (a pause on the host, such as the end
+    of a timed loop).  With ``timed`` only the runs that bench.py's phase
+    markers enclose (a one-workgroup K = 0 launch before, a two-workgroup
+    one after) are reported, whole: exactly the timed launches of each
+    workload."""
     with open(path) as f:
         rows_in = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
     runs = []
+    prev_end = None
     for r in rows_in:
         key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
-        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if runs and runs[-1][0] == key:
+        start, end = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        us = (end - start) / 1e3
+        idle = gap_ms > 0 and prev_end is not None and start - prev_end > gap_ms * 1e6
+        prev_end = end if prev_end is None else max(prev_end, end)
+        if runs and runs[-1][0] == key and not idle:
             runs[-1][1].append(us)
         else:
             runs.append((key, [us]))
+    if timed:
+        shaped = [((k[0], k[1] // max(k[2], 1)), v) for k, v in runs]
+        runs = [runs[i] for i in range(len(runs))
+                if not shaped[i][0][0].startswith(MARKER_KERNEL) and
+                _marker_index(shaped, i - 1, 1) and _marker_index(shaped, i + 1, 2)]
     if last > 0:
         runs = [(k, v[-last:]) for k, v in runs if len(v) >= last]
     total = sum(sum(v) for _, v in runs)
@@ -174,7 +199,8 @@ def counter_runs(paths, labels, last: int = 8, kernels=("bf16_q4", "fp8_q4")):
     """Median counter values per workload from one or more --pmc passes of
     the same bench command: each pass's dispatches are split into runs of
     consecutive dispatches of one kernel and launch shape (one run per
-    workload, as in dispatch_stats), runs of the named kernel families with
+    workload, as in dispatch_stats; where bench.py's phase markers are
+    present, only the timed runs they enclose), runs of the named kernel families with
     at least 5 dispatches are matched in order to ``labels``, and every
     counter is the median over the last ``last`` dispatches of its run
     (summed over the device).  Returns {label: {counter: value, "us": ...}}."""
@@ -200,6 +226,11 @@ def counter_runs(paths, labels, last: int = 8, kernels=("bf16_q4", "fp8_q4")):
                 runs[-1][1].append(disp[d])
             else:
                 runs.append((k, [disp[d]]))
+        enclosed = [runs[i] for i in range(len(runs))
+                    if not runs[i][0][0].startswith(MARKER_KERNEL) and
+                    _marker_index(runs, i - 1, 1) and _marker_index(runs, i + 1, 2)]
+        if enclosed:  # bench.py's phase markers: keep exactly the timed launches
+            runs = enclosed
         runs = [(k, v) for k, v in runs if len(v) >= 5 and
                 (k[0].startswith(tuple(kernels)) if kernels else not k[0].startswith("__amd"))]
         for label, (k, v) in zip(labels, runs):
@@ -319,6 +350,10 @@ def main():
     t = sub.add_parser("trace", help="markdown table per kernel and launch shape from "
                        "--kernel-trace output")
     t.add_argument("dir")
+    t.add_argument("--timed", action="store_true",
+                   help="only the runs bench.py's phase markers enclose: its timed launches")
+    t.add_argument("--gap-ms", type=float, default=0.0,
+                   help="also end a run where the device sat idle longer than this")
     t.add_argument("--last", type=int, default=0,
                    help="report runs of at least N consecutive dispatches by their last N "
                    "(steady state)")
@@ -370,7 +405,8 @@ def main():
         print(account_markdown(runs))
         return
     if args.cmd == "trace":
-        print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"), args.last)))
+        print(stats_markdown(dispatch_stats(_find(args.dir, "_kernel_trace.csv"), args.last,
+                                            args.gap_ms, args.timed)))
         return
     fetch = counter_medians(_find(args.fetch, "_counter_collection.csv"))
     write = counter_medians(_find(args.write, "_counter_collection.csv"))

@@ -110,3 +110,27 @@ def test_lds_probe_rows_groups_by_stride(tmp_path):
     assert [r["stride"] for r in rows] == [1, 2, 4]
     assert [r["extra_per_cycle"] for r in rows] == [0.0, 1.0, 3.0]
     assert [r["us"] for r in rows] == [1.0, 2.0, 4.0]
+
+
+def test_dispatch_stats_timed_runs_between_markers(tmp_path):
+    """bench.py's phase markers (a one-workgroup K = 0 launch before, a
+    two-workgroup one after each timed loop): --timed keeps exactly the
+    enclosed runs, whole, not the warm-ups or what follows a loop."""
+    from roofline_driven_optimisation_amd.profiling import dispatch_stats
+    k = "void gemm_kernel<true>(float*) [clone .kd]"
+    mark = "void mgemm::(anonymous namespace)::scale_kernel<false>(unsigned long, int, float, float*)"
+    close = mark + " "  # the same kernel; the marker after a timed loop has two workgroups
+    seq = ([(k, 9.0)] * 30 + [(mark, 1.0)] + [(k, 4.0)] * 20 + [(close, 1.0)] + [(k, 6.0)] * 40
+           + [(mark, 1.0)] + [(k, 5.0)] * 10 + [(close, 1.0)])
+    rows, t = [], 0
+    for name, us in seq:
+        grid = {mark: 256, close: 512}.get(name, 65536)
+        rows.append((name, grid, 256, t, t + int(us * 1000)))
+        t += 20000
+    path = tmp_path / "t_kernel_trace.csv"
+    _trace_csv(path, rows)
+    timed = dispatch_stats(str(path), timed=True)
+    # the 40 launches after the first closing marker are the next warm-up:
+    # a closing marker before them, not an opening one
+    assert [(r["calls"], r["avg_us"]) for r in timed] == [(20, 4.0), (10, 5.0)]
+    assert [r["calls"] for r in dispatch_stats(str(path))] == [30, 1, 20, 1, 40, 1, 10, 1]
