@@ -277,40 +277,32 @@ __device__ __forceinline__ void store_c_tile_lds(const f32x16 (&acc)[MI][NI], fl
     }
 }
 
-// Epilogue through LDS for a wave tile 128 columns wide (MI blocks of 32
-// rows): one block row at a time, the wave writes its 32 x 128 fp32 values
-// into a private 16 KB LDS region (16-byte chunk c of row r at position
-// c ^ (r % 16), so the 16 lanes served together hit 64 distinct banks both
-// when writing and when reading back), reads them back two rows per
-// instruction and stores them with 32 lanes per 512-byte row segment: each
-// store instruction covers 8 whole 128-byte lines.  C = alpha * acc (+ beta
-// * C); same edge handling as store_c_tile.  MODE and PLOAD as for
+// Epilogue through LDS for a wave tile 128 columns wide, 32 rows (a band)
+// at a time: write_band(i, region) puts band i of the wave's fp32 values into
+// a private 16 KB LDS region (16-byte chunk c of row r at position c ^ (r %
+// 16), so the 16 lanes served together hit 64 distinct banks both when
+// writing and when reading back); the band is read back two rows per
+// instruction and stored with 32 lanes per 512-byte row segment: each store
+// instruction covers 8 whole 128-byte lines.  C = alpha * acc (+ beta * C);
+// same edge handling as store_c_tile.  MODE and PLOAD as for
 // store_c_tile_lds (a partial tile `rw` of ldw floats per row).
-template <int MI, EpilogueMode MODE = kStoreC, int PLOAD = kSystemScope, bool EPI = false>
-__device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], float *region,
-                                                    __amdgpu_buffer_rsrc_t rc, int row0,
-                                                    int col0, int cols_left, int N, float alpha,
-                                                    float beta, __amdgpu_buffer_rsrc_t rw,
-                                                    int ldw, const float *bias = nullptr,
-                                                    int act = kActNone) {
+template <int BANDS, EpilogueMode MODE = kStoreC, int PLOAD = kSystemScope, bool EPI = false,
+          class WriteBand>
+__device__ __forceinline__ void store_c_bands_lds128(WriteBand &&write_band, float *region,
+                                                     __amdgpu_buffer_rsrc_t rc, int row0,
+                                                     int col0, int cols_left, int N, float alpha,
+                                                     float beta, __amdgpu_buffer_rsrc_t rw,
+                                                     int ldw, const float *bias = nullptr,
+                                                     int act = kActNone) {
     const int lane = threadIdx.x & 63;
-    const int l32 = lane & 31, h = lane >> 5;
+    const int h = lane >> 5;
     const bool read_c = beta != 0.0f;
     // a lane stores the same four columns in every pass: their bias is
     // loaded once, before any store (a load after a store to C would wait)
     const f32x4 bv = bias4<EPI && MODE != kPostPartial>(bias, col0 + 4 * (lane & 31), cols_left);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int chunk = 8 * jj + 2 * g + h;
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][jj][4 * g + e];
-                *reinterpret_cast<f32x4 *>(&region[l32 * 128 + ((chunk ^ (l32 & 15)) * 4)]) = v;
-            }
+    for (int i = 0; i < BANDS; ++i) {
+        write_band(i, region);
         const int chunk = lane & 31;
         const int col = col0 + 4 * chunk;
         // The rows' global loads (partial, C) are issued a group at a time
@@ -396,6 +388,38 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
             });
         }
     }
+}
+
+// Band i of a wave's MI x 4 blocks of 32 x 32 (the transposed layout of
+// store_c_tile): register 4 g + e of lane l holds row l % 32, column 32 jj +
+// 8 g + 4 (l / 32) + e of block (i, jj), i.e. 16-byte chunk 8 jj + 2 g + l / 32.
+template <int MI>
+__device__ __forceinline__ auto band_writer32(const f32x16 (&acc)[MI][4]) {
+    return [&acc](int i, float *region) {
+        const int lane = threadIdx.x & 63;
+        const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int chunk = 8 * jj + 2 * g + h;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][jj][4 * g + e];
+                *reinterpret_cast<f32x4 *>(&region[l32 * 128 + ((chunk ^ (l32 & 15)) * 4)]) = v;
+            }
+    };
+}
+
+template <int MI, EpilogueMode MODE = kStoreC, int PLOAD = kSystemScope, bool EPI = false>
+__device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], float *region,
+                                                    __amdgpu_buffer_rsrc_t rc, int row0,
+                                                    int col0, int cols_left, int N, float alpha,
+                                                    float beta, __amdgpu_buffer_rsrc_t rw,
+                                                    int ldw, const float *bias = nullptr,
+                                                    int act = kActNone) {
+    store_c_bands_lds128<MI, MODE, PLOAD, EPI>(band_writer32<MI>(acc), region, rc, row0, col0,
+                                               cols_left, N, alpha, beta, rw, ldw, bias, act);
 }
 
 template <int BM, int BN, bool KTAIL, bool EPI>
@@ -1004,18 +1028,19 @@ __global__ __launch_bounds__(512, 1) void bf16_pp_kernel(int M, int N, int K, fl
 // to the pair's workspace slot and publishes it, split 1 waits for it
 // (pair_wait: on time-out it writes NaN rather than hang) and stores alpha
 // (acc + partial) + beta C.  `word` is an LDS int the workgroup no longer
-// uses (it broadcasts the wait's outcome).
-template <int MI, bool EPI>
-__device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], float *region,
-                                                 __amdgpu_buffer_rsrc_t rc, int row0, int col0,
-                                                 int cols_left, int N, float alpha, float beta,
-                                                 int split, int v, const PPSplit &split_plan,
-                                                 const float *bias, int act, int *word) {
+// uses (it broadcasts the wait's outcome).  The wave's accumulators reach
+// the epilogue through write_band (see store_c_bands_lds128).
+template <int BANDS, bool EPI, class WriteBand>
+__device__ __forceinline__ void store_split_bands(WriteBand &&wb, float *region,
+                                                  __amdgpu_buffer_rsrc_t rc, int row0, int col0,
+                                                  int cols_left, int N, float alpha, float beta,
+                                                  int split, int v, const PPSplit &split_plan,
+                                                  const float *bias, int act, int *word) {
     constexpr int BN = kPPTile;
     if (split < 0) {
-        store_c_tile_lds128<MI, kStoreC, kSystemScope, EPI>(acc, region, rc, row0, col0,
-                                                            cols_left, N, alpha, beta, rc, 0,
-                                                            bias, act);
+        store_c_bands_lds128<BANDS, kStoreC, kSystemScope, EPI>(wb, region, rc, row0, col0,
+                                                                cols_left, N, alpha, beta, rc, 0,
+                                                                bias, act);
         return;
     }
     const int slot = v - split_plan.split_from;
@@ -1023,8 +1048,8 @@ __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], flo
         make_rsrc(split_plan.partials + static_cast<size_t>(slot) * BN * BN, BN * BN * 4);
     const bool local = split_plan.xcd_pairs != 0;
     if (split == 0) {
-        store_c_tile_lds128<MI, kPostPartial>(acc, region, rc, row0, col0, cols_left, N, alpha,
-                                              beta, rw, BN);
+        store_c_bands_lds128<BANDS, kPostPartial>(wb, region, rc, row0, col0, cols_left, N,
+                                                  alpha, beta, rw, BN);
         if (local)
             pair_publish<true>(split_plan, slot);
         else
@@ -1035,11 +1060,21 @@ __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], flo
                           : pair_wait<false>(split_plan, slot, word);
     const float a = ok ? alpha : __builtin_nanf("");
     if (local)
-        store_c_tile_lds128<MI, kAddPartial, kDeviceScope, EPI>(
-            acc, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
+        store_c_bands_lds128<BANDS, kAddPartial, kDeviceScope, EPI>(
+            wb, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
     else
-        store_c_tile_lds128<MI, kAddPartial, kSystemScope, EPI>(
-            acc, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
+        store_c_bands_lds128<BANDS, kAddPartial, kSystemScope, EPI>(
+            wb, region, rc, row0, col0, cols_left, N, a, beta, rw, BN, bias, act);
+}
+
+template <int MI, bool EPI>
+__device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], float *region,
+                                                 __amdgpu_buffer_rsrc_t rc, int row0, int col0,
+                                                 int cols_left, int N, float alpha, float beta,
+                                                 int split, int v, const PPSplit &split_plan,
+                                                 const float *bias, int act, int *word) {
+    store_split_bands<MI, EPI>(band_writer32<MI>(acc), region, rc, row0, col0, cols_left, N, alpha,
+                               beta, split, v, split_plan, bias, act, word);
 }
 
 // ---------------------------------------------------------------------------
@@ -1300,12 +1335,299 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
 }
 
 
+// ---------------------------------------------------------------------------
+// The four-wave 256 x 256 kernel on the 16 x 16 x 32 matrix instruction
+// (v_mfma_f32_16x16x32_bf16): same tile, K step 32, four LDS stages and
+// copies three steps ahead, but each wave's 128 x 128 tile is 8 x 8 blocks
+// of 16 x 16 (four fp32 accumulators per lane per block, still 256 in all)
+// and one MFMA covers a whole K step.  The two instructions do the same work
+// per cycle at the same operand bytes per MFMA cycle; on gfx950 the board
+// holds a higher clock under a stream of the smaller one.
+//
+// Fragments (lane l, group g = l / 16): an A fragment is row l % 16 of a
+// block, k = 8 g .. 8 g + 7, one 16-byte read (A stage as in the 32 x 32
+// kernel); a B fragment is column l % 16, the same k: two transposing reads
+// of 4 k rows each.  The 32 lanes of a transposing
+// read then cover rows 8 g' + 0..3 for g' in {g, g + 1} (not 4 consecutive
+// rows, as in the 32 x 32 kernel), 32 bytes per row; the B swizzle key gains
+// a bit from k / 8 (swz_b16) so those 8 rows fall on the 8 different
+// 32-byte quarters of a bank line.  The MFMAs take B's fragment first: lane
+// l holds row l % 16, columns 4 g .. 4 g + 3 of its block, one 16-byte chunk
+// of the epilogue's staging layout.
+//
+// One set of fragment registers, and a step's 64 MFMAs in two halves: A
+// blocks 0 .. 3 with every B block, then A blocks 4 .. 7 with every B block
+// (B-major inside a half: MFMA 32 h + 4 jj + i' is block (4 h + i', jj)).
+// A fragments 0 .. 3 are then free after MFMA 31, B fragment jj after MFMA
+// 35 + 4 jj and A fragments 4 .. 7 after MFMA 63, and each is read again
+// for the next step soon after, so the reads spread over the whole step:
+//   * first half of step t: the reads of step t's B blocks 6 and 7 and A
+//     blocks 4 .. 7, and the last 4 copies of step t + 3, one per 8 MFMAs;
+//   * then the wait (step t + 1's copies landed, every read of step t done)
+//     and the workgroup barrier;
+//   * second half: the reads of step t + 1's A blocks 0 .. 3 and B blocks
+//     0 .. 5, each right after its last use (B blocks 6 and 7 wait for the
+//     next half: read at the end of this one, they would hold up the next
+//     step's first MFMA, which waits for every read of the previous step),
+//     and the first 4 copies of step t + 4, one per 8 MFMAs.
+// So the reads of stage t run from the barrier of step t - 1 to that of
+// step t, and the copies into its stage (for step t + 4) start after the
+// barrier that ends those reads.  Spreading the copies over the whole step
+// matters more here than with the 32 x 32 instruction: a 16 x 16 MFMA leaves
+// the wave a third as many cycles to issue between MFMAs, and a burst of
+// copies (all 8 in one half step) kept the texture unit's address queue
+// full, stalling the copy instructions and the MFMAs behind them.
+__device__ __forceinline__ int swz_b16(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 1); }
+
+template <bool KTAIL, bool EPI, bool TRANSB>
+__global__ __launch_bounds__(256, 1) void bf16_q16_kernel(int M, int N, int K, float alpha,
+                                                          float beta,
+                                                          const uint16_t *__restrict__ A,
+                                                          const uint16_t *__restrict__ B, float *C,
+                                                          int tiles_m, int tiles_n,
+                                                          PPSplit split_plan, Epi epi,
+                                                          Batch batch) {
+    constexpr int BM = 256, BN = 256, S = 4, BK = kPPBK;
+    constexpr int WM = 128, WN = 128, MI = 8, NI = 8;  // 16 x 16 blocks per wave
+    constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;
+    constexpr int A_LOADS = BM / 16 / 4;
+    constexpr int B_ROWS = 512 / BN;
+    constexpr int B_LOADS = BK / B_ROWS / 4;
+    constexpr int COPIES = A_LOADS + B_LOADS;
+    constexpr int B_CHUNKS = BN / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][A_STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][B_STAGE];
+
+    int v, split;
+    __shared__ int s_words[2];
+    split_tile(blockIdx.x, split_plan, v, split, &s_words[0]);
+    const int per_item = tiles_m * tiles_n;
+    const int item = v / per_item;
+    A += item * batch.stride_a;
+    B += item * batch.stride_b;
+    C += item * batch.stride_c;
+    int tm, tn;
+    grouped_tile(v - item * per_item, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int total_steps = (K + BK - 1) / BK;
+    const int t_begin = split == 1 ? split_plan.split_step : 0;
+    const int t_end = split == 0 ? split_plan.split_step : total_steps;
+    const int T = t_end - t_begin;  // this workgroup's steps; t below counts them
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // A copies as in the 32 x 32 kernel.  B copies (B as K x N): copy q of a
+    // wave fills rows 8 q + 2 wave + l / 32, whose key differs between even
+    // and odd q (bit 3 of the row), so a lane has two source chunks.
+    const int a_row_in = lane >> 2;
+    const int a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t a_off = static_cast<uint32_t>(((16 * wave + a_row_in) * K + 8 * a_chunk) * 2);
+    const uint32_t a_step = static_cast<uint32_t>(64 * K * 2);
+    const int b_row0 = B_ROWS * wave + lane / B_CHUNKS;
+    const int b_c0 = (lane % B_CHUNKS) ^ swz_b16(b_row0);
+    const int b_c1 = (lane % B_CHUNKS) ^ swz_b16(b_row0 + 8);
+    const bool b_ok0 = (n0 + 8 * b_c0) < N, b_ok1 = (n0 + 8 * b_c1) < N;
+    const uint32_t b_off0 = static_cast<uint32_t>((b_row0 * N + 8 * b_c0) * 2);
+    const uint32_t b_off1 = static_cast<uint32_t>((b_row0 * N + 8 * b_c1) * 2);
+    const uint32_t b_step = static_cast<uint32_t>(4 * B_ROWS * N * 2);
+    static_assert(!TRANSB || B_LOADS == A_LOADS, "a transposed B tile copies like A's");
+
+    struct StepCopy {
+        i32x4 ra, rb;
+        uint32_t la, lb;
+        bool a_ok;
+    };
+    auto step_copy = [&](int t) {
+        const int k0 = (t_begin + t) * BK, stage = t % S;
+        StepCopy c;
+        c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                         (static_cast<long long>(M - m0) * K - k0) * 2);
+        if constexpr (TRANSB)
+            c.rb = make_desc(B + static_cast<size_t>(n0) * K + k0,
+                             (static_cast<long long>(N - n0) * K - k0) * 2);
+        else
+            c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                             (static_cast<long long>(K - k0) * N - n0) * 2);
+        c.a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
+        c.la = lds_address(&lds_a[stage][wave * 512]);
+        c.lb = lds_address(&lds_b[stage][wave * 512]);
+        return c;
+    };
+    auto issue_copy = [&](const StepCopy &c, int q) {
+        const int r = q - A_LOADS;
+        if (q < A_LOADS)
+            lds_dma16(c.ra, c.la + q * 4 * 1024, c.a_ok ? a_off + q * a_step : kOOB);
+        else if constexpr (TRANSB)
+            lds_dma16(c.rb, c.lb + r * 4 * 1024, c.a_ok ? a_off + r * a_step : kOOB);
+        else if (r & 1)
+            lds_dma16(c.rb, c.lb + r * 4 * 1024, b_ok1 ? b_off1 + r * b_step : kOOB);
+        else
+            lds_dma16(c.rb, c.lb + r * 4 * 1024, b_ok0 ? b_off0 + r * b_step : kOOB);
+    };
+
+    const int r16 = lane & 15, g = lane >> 4;
+    const int a_lane_base = (wm * WM + r16) * BK;
+    const int a_pos = (g ^ swz_a32(r16)) * 8;
+    const int b_col_lane = wn * WN + 4 * (r16 & 3);
+    const int b_row_lane = 8 * g + (r16 >> 2);
+    const int bt_lane_base = (wn * WN + r16) * BK;  // TRANSB: row n of the B tile
+    bf16x8 fa[MI];
+    u32x4 fb[NI];  // filled a dword pair at a time (16-bit inserts cost a wait on the read)
+    auto read_a = [&](int stage, int i) {
+        const u32x4 x =
+            *reinterpret_cast<const u32x4 *>(&lds_a[stage][a_lane_base + 16 * i * BK + a_pos]);
+        fa[i] = __builtin_bit_cast(bf16x8, x);
+    };
+    // B fragment jj: one plain read (TRANSB) or transposing read r of two
+    auto read_b = [&](int stage, int jj, int r) {
+        if constexpr (TRANSB) {
+            fb[jj] = *reinterpret_cast<const u32x4 *>(
+                &lds_b[stage][bt_lane_base + 16 * jj * BK + a_pos]);
+        } else {
+            const int row = 4 * r + b_row_lane;
+            const int col = b_col_lane + 16 * jj;
+            const int chunk = (col >> 3) ^ swz_b16(row);
+            const int elem = row * BN + chunk * 8 + (col & 7);
+            const u32x2 part = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (s16x4 __attribute__((address_space(3))) *)&lds_b[stage][elem]));
+            fb[jj][2 * r] = part[0];
+            fb[jj][2 * r + 1] = part[1];
+        }
+    };
+    constexpr int kBReads = TRANSB ? 1 : 2;  // reads per B fragment
+
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][jj][e] = 0.0f;
+    constexpr int kHalf = MI * NI / 2;
+    auto mfma = [&](int q) {
+        const int h = q / kHalf, jj = (q % kHalf) / 4, i = 4 * h + q % 4;
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[jj]),
+                                                             fa[i], acc[i][jj], 0, 0, 0);
+    };
+    constexpr int kHalfCopies = COPIES / 2;  // per half step, one per 8 MFMAs
+    static_assert(8 * kHalfCopies <= kHalf, "the copies fit a half step");
+    constexpr int kWaitSteady = (2 * COPIES & 15) | (7 << 4) | ((2 * COPIES >> 4) << 14);
+    constexpr int kWaitDrain = (7 << 4);
+
+    // steps 0 .. 2 and the first half of step 3's copies (which a second
+    // half issues in the steady state)
+    for (int t = 0; t < S - 1; ++t)
+        if (t < T) {
+            const StepCopy c = step_copy(t);
+#pragma unroll
+            for (int q = 0; q < COPIES; ++q) issue_copy(c, q);
+        }
+    if (T > S - 1) {
+        const StepCopy c = step_copy(S - 1);
+#pragma unroll
+        for (int q = 0; q < kHalfCopies; ++q) issue_copy(c, q);
+        __builtin_amdgcn_s_waitcnt(wait_vm(2 * COPIES + kHalfCopies));  // step 0 landed
+    } else {
+        __builtin_amdgcn_s_waitcnt(kWaitDrain);
+    }
+    __syncthreads();
+    // what a second half reads for the next step, here for step 0 with no
+    // MFMA to hide it
+    if (T > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) read_a(0, i);
+#pragma unroll
+        for (int jj = 0; jj < NI - 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < kBReads; ++r) read_b(0, jj, r);
+    }
+
+    // step t; COPY1: issue the second half of step t + 3's copies, COPY2:
+    // the first half of step t + 4's (into the stage step t reads, after the
+    // barrier that ends those reads); NEXT: read step t + 1
+    auto k_step = [&](int t, auto copy1_tag, auto copy2_tag, auto next_tag) {
+        constexpr bool COPY1 = decltype(copy1_tag)::value;
+        constexpr bool COPY2 = decltype(copy2_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int cur = t % S, nxt = (t + 1) % S;
+        StepCopy c;
+        if constexpr (COPY1) c = step_copy(t + S - 1);
+#pragma unroll
+        for (int q = 0; q < kHalf; ++q) {
+            mfma(q);
+            // B blocks 6 and 7 first (their last uses closed step t - 1),
+            // then A blocks 4 .. 7, one per two MFMAs
+            if (q < 2 * kBReads) read_b(cur, NI - 2 + q / kBReads, q % kBReads);
+            if (q >= 4 && q < 12 && (q & 1) == 0) read_a(cur, 4 + (q - 4) / 2);
+            if constexpr (COPY1) {
+                if ((q & 7) == 3) issue_copy(c, kHalfCopies + q / 8);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(COPY1 ? kWaitSteady : kWaitDrain);
+        __syncthreads();
+        StepCopy c2;
+        if constexpr (COPY2) c2 = step_copy(t + S);
+#pragma unroll
+        for (int q = kHalf; q < 2 * kHalf; ++q) {
+            mfma(q);
+            if constexpr (NEXT) {
+                const int u = q - kHalf;  // MFMA u of the second half uses B block u / 4
+                if (u < 4) read_a(nxt, u);  // A blocks 0 .. 3: last used in the first half
+                if (u % 4 == 3 && u / 4 < NI - 2) {  // B block u / 4: this was its last use
+#pragma unroll
+                    for (int r = 0; r < kBReads; ++r) read_b(nxt, u / 4, r);
+                }
+            }
+            if constexpr (COPY2) {
+                if ((q & 7) == 3) issue_copy(c2, (q - kHalf) / 8);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using On = std::true_type;
+    using Off = std::false_type;
+    int t = 0;
+    for (; t < T - S; ++t) k_step(t, On(), On(), On());  // steps t + 3 and t + 4 exist
+    if (t == T - S) {
+        k_step(t, On(), Off(), On());
+        ++t;
+    }
+    for (; t < T - 1; ++t) k_step(t, Off(), Off(), On());
+    if (T > 0) k_step(T - 1, Off(), Off(), Off());
+    // the epilogue stages through the A stages: every wave's last reads are
+    // done (the barrier inside the last step), and no copy is in flight
+
+    // epilogue: band i holds block rows 2 i and 2 i + 1; lane l writes row
+    // 16 rb + l % 16, chunk 4 jj + l / 16 of each block (rb, jj) of the band
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + static_cast<size_t>(m0) * N + n0,
+                  (static_cast<long long>(M - m0) * N - n0) * 4);
+    static_assert(S * A_STAGE * 2 >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
+    float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
+    auto write_band = [&](int i, float *reg) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj) {
+                const int r = 16 * rb + r16, chunk = 4 * jj + g;
+                *reinterpret_cast<f32x4 *>(&reg[r * 128 + ((chunk ^ r16) * 4)]) = acc[2 * i + rb][jj];
+            }
+    };
+    const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
+    store_split_bands<MI / 2, EPI>(write_band, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta,
+                                   split, v, split_plan, bias, epi.act, &s_words[1]);
+}
+
 const Bf16TileConfig kConfigs[] = {
     {256, 256, "bf16_q4_256x256x32"},
     {256, 128, "bf16_mfma_256x128x64"},
     {128, 256, "bf16_mfma_128x256x64"},
     {128, 128, "bf16_mfma_128x128x64"},
     {256, 256, "bf16_pp_256x256x32"},
+    {256, 256, "bf16_q16_256x256x32"},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1314,11 +1636,11 @@ constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 // unit).  At 4096^3 the four-wave 256 x 256 kernel ran 0.5-2.7 us ahead of
 // the ping-pong kernel on three boards out of four, and with a split last
 // round 1.5-4 us ahead on the four 2048-row prefill shapes.
-const double kTileEfficiency[kNumConfigs] = {1.29, 0.85, 0.85, 1.0, 1.27};
+const double kTileEfficiency[kNumConfigs] = {1.29, 0.85, 0.85, 1.0, 1.27, 1.20};
 // LDS bytes per workgroup, which set how many workgroups share a CU.
 int tile_lds_bytes(int c) {
     const Bf16TileConfig &t = kConfigs[c];
-    return (c == 0 || c == 4) ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
+    return (c == 0 || c == 4 || c == 5) ? 4 * (t.bm + t.bn) * 32 * 2 : 2 * (t.bm + t.bn) * 64 * 2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1612,6 +1934,7 @@ bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan, int 
     return true;
 }
 
+template <bool Q16>
 hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                      const uint16_t *B, float *C, const PPSplit *split, const Epi &epi,
                      hipStream_t stream, const Batch &batch = kOneItem, bool trans_b = false) {
@@ -1624,10 +1947,18 @@ hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_
     if (!make_plan(split, total, K, plan)) return hipErrorInvalidValue;
     const long long grid = plan.split_from + 2 * (total - plan.split_from);
     auto go = [&](auto ktail, auto e, auto tb) {
-        bf16_q4_kernel<decltype(ktail)::value, decltype(e)::value, decltype(tb)::value>
-            <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
-                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
-                static_cast<int>(tiles_n), plan, epi, batch);
+        constexpr bool KT = decltype(ktail)::value, EP = decltype(e)::value,
+                       TB = decltype(tb)::value;
+        if constexpr (Q16)
+            bf16_q16_kernel<KT, EP, TB><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                                          stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                    static_cast<int>(tiles_m),
+                                                    static_cast<int>(tiles_n), plan, epi, batch);
+        else
+            bf16_q4_kernel<KT, EP, TB><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                                         stream>>>(M, N, K, alpha, beta, A, B, C,
+                                                   static_cast<int>(tiles_m),
+                                                   static_cast<int>(tiles_n), plan, epi, batch);
     };
     if (trans_b) {
         if (epi_on(epi)) return hipErrorInvalidValue;  // no fused epilogue in batched calls
@@ -1683,7 +2014,15 @@ const Bf16TileConfig &bf16_tile_config(int cfg) { return kConfigs[cfg]; }
 
 int bf16_pp_config() { return 4; }
 
-bool bf16_config_splits(int cfg) { return cfg == 0 || cfg == 4; }
+bool bf16_config_splits(int cfg) { return cfg == 0 || cfg == 4 || cfg == 5; }
+
+const char *bf16_split_name(int cfg, bool xcd_pairs) {
+    switch (cfg) {
+        case 4: return xcd_pairs ? "bf16_pp_256x256x32_splitk_xcd" : "bf16_pp_256x256x32_splitk";
+        case 5: return xcd_pairs ? "bf16_q16_256x256x32_splitk_xcd" : "bf16_q16_256x256x32_splitk";
+        default: return xcd_pairs ? "bf16_q4_256x256x32_splitk_xcd" : "bf16_q4_256x256x32_splitk";
+    }
+}
 
 int bf16_pp_split_tiles(int M, int N, int K, int num_cus) {
     // Split the last round when it is at most half full and each half of K
@@ -1769,8 +2108,11 @@ hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float 
                                bool trans_b, hipStream_t stream) {
     switch (cfg) {
         case 0:
-            return launch_q4(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
-                             trans_b);
+            return launch_q4<false>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
+                                    trans_b);
+        case 5:
+            return launch_q4<true>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
+                                   trans_b);
         case 3:
             if (trans_b) return hipErrorInvalidValue;
             return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, kNoEpi, stream, batch);
@@ -1783,7 +2125,8 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
                             const Epi &epi, hipStream_t stream) {
     if (split != nullptr && !bf16_config_splits(cfg)) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return launch_q4(M, N, K, alpha, beta, A, B, C, split, epi, stream);
+        case 0: return launch_q4<false>(M, N, K, alpha, beta, A, B, C, split, epi, stream);
+        case 5: return launch_q4<true>(M, N, K, alpha, beta, A, B, C, split, epi, stream);
         case 1: return launch_cfg<256, 128>(M, N, K, alpha, beta, A, B, C, epi, stream);
         case 2: return launch_cfg<128, 256>(M, N, K, alpha, beta, A, B, C, epi, stream);
         case 3: return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, epi, stream);

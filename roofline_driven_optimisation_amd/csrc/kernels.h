@@ -102,6 +102,7 @@ struct PPSplit {
 };
 int bf16_pp_config();                                          // the ping-pong tile index
 bool bf16_config_splits(int cfg);  // the 256 x 256 kernels, which can split a last round
+const char *bf16_split_name(int cfg, bool xcd_pairs);  // kernel name of a split launch
 int bf16_pp_split_tiles(int M, int N, int K, int num_cus);    // 0: no split
 hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float beta,
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,

@@ -60,6 +60,11 @@ BF16_PATHS = [
     ((520, 776, 328), {"MGEMM_BF16_TILE": "bf16_pp_256x256x32"}, "bf16_pp_256x256x32_splitk"),
     ((512, 768, 320), {"MGEMM_BF16_TILE": "bf16_pp_256x256x32", "MGEMM_PP_SPLIT": "0"},
      "bf16_pp_256x256x32"),
+    ((512, 768, 320), {"MGEMM_BF16_TILE": "bf16_q16_256x256x32", "MGEMM_PP_SPLIT": "0"},
+     "bf16_q16_256x256x32"),
+    ((520, 776, 328), {"MGEMM_BF16_TILE": "bf16_q16_256x256x32"}, "bf16_q16_256x256x32_splitk"),
+    ((1024, 4096, 264), {"MGEMM_BF16_TILE": "bf16_q16_256x256x32"},
+     "bf16_q16_256x256x32_splitk_xcd"),
     ((300, 264, 200), {"MGEMM_BF16_TILE": "bf16_mfma_256x128x64"}, "bf16_mfma_256x128x64"),
     ((300, 264, 200), {"MGEMM_BF16_TILE": "bf16_mfma_128x256x64"}, "bf16_mfma_128x256x64"),
     ((300, 264, 200), {"MGEMM_BF16_TILE": "bf16_mfma_128x128x64"}, "bf16_mfma_128x128x64"),
@@ -106,7 +111,7 @@ def test_f32_epilogue(path, act, monkeypatch):
 
 
 @pytest.mark.parametrize("act", [binding.ACT_NONE, binding.ACT_RELU], ids=["none", "relu"])
-@pytest.mark.parametrize("path", BF16_PATHS[:12], ids=lambda p: p[2] + "_" + "x".join(map(str, p[0])))
+@pytest.mark.parametrize("path", BF16_PATHS[:-2], ids=lambda p: p[2] + "_" + "x".join(map(str, p[0])))
 def test_bf16_epilogue_exact_integers(path, act, monkeypatch):
     """Integer A, B, C and bias: every sum is exact in fp32, so identity and
     ReLU results equal the oracle's bit for bit."""

@@ -74,7 +74,8 @@ def test_decode_fresh_stream_one_split(torch):
     assert name == "skinny_bf16", name
 
 
-@pytest.mark.parametrize("tile", ["bf16_pp_256x256x32", "bf16_q4_256x256x32"])
+@pytest.mark.parametrize("tile", ["bf16_pp_256x256x32", "bf16_q4_256x256x32",
+                                  "bf16_q16_256x256x32"])
 def test_pp_split_shape_unsplit_under_capture(torch, tile, monkeypatch):
     """A shape whose last round would be split runs whole tiles when captured."""
     monkeypatch.setenv("MGEMM_BF16_TILE", tile)

@@ -241,7 +241,7 @@ def test_deterministic_repeat(gpu):
 
 
 TILE_NAMES = ["bf16_q4_256x256x32", "bf16_mfma_256x128x64", "bf16_mfma_128x256x64",
-              "bf16_mfma_128x128x64", "bf16_pp_256x256x32"]
+              "bf16_mfma_128x128x64", "bf16_pp_256x256x32", "bf16_q16_256x256x32"]
 
 
 @pytest.mark.parametrize("tile", TILE_NAMES)
@@ -294,7 +294,7 @@ def test_skinny_splits(splits, shape, xcd, monkeypatch):
     check_full(case, C)
 
 
-SPLIT_TILES = ["bf16_pp_256x256x32", "bf16_q4_256x256x32"]
+SPLIT_TILES = ["bf16_pp_256x256x32", "bf16_q4_256x256x32", "bf16_q16_256x256x32"]
 
 
 @pytest.mark.parametrize("tile", SPLIT_TILES)
@@ -327,13 +327,14 @@ def test_pp_split_tail(shape, xcd, tile, monkeypatch):
 
 
 def test_pp_split_alternating(monkeypatch):
-    """Split calls alternating between the two 256 x 256 kernels, between
+    """Split calls alternating between the three 256 x 256 kernels, between
     XCD-local and cross-XCD pairs, and between shapes, share the flag epochs
     of one stream: every call exact."""
     monkeypatch.setenv("MGEMM_DISABLE_SKINNY", "1")
     plan = [((1024, 4096, 264), "1", 0), ((1024, 4096, 264), "0", 1), ((512, 2048, 328), "1", 1),
             ((500, 712, 320), "1", 0), ((1024, 4096, 264), "1", 1), ((512, 2048, 328), "0", 0),
-            ((500, 712, 320), "0", 1), ((1024, 4096, 264), "1", 0)]
+            ((500, 712, 320), "0", 1), ((1024, 4096, 264), "1", 0), ((512, 2048, 328), "1", 2),
+            ((1024, 4096, 264), "0", 2), ((500, 712, 320), "1", 1)]
     for i, (shape, xcd, k) in enumerate(plan):
         monkeypatch.setenv("MGEMM_PP_XCD", xcd)
         monkeypatch.setenv("MGEMM_BF16_TILE", SPLIT_TILES[k])
