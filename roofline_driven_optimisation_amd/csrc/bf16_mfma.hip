@@ -1903,6 +1903,235 @@ __global__ __launch_bounds__(256, 1) void fp8_q4_kernel(int M, int N, int K, flo
                                 v, split_plan, nullptr, kActNone, &s_words[1]);
 }
 
+// ---------------------------------------------------------------------------
+// The 8-bit float GEMM with a 128-deep K step: the same 256 x 256 tile, four
+// waves, 128 x 128 wave tiles and v_mfma_scale_f32_32x32x64_f8f6f4, but each
+// step copies 128 bytes of every A and B row, a whole 128-byte line, where
+// the 64-deep kernel above copies half lines (64 bytes of each of twice as
+// many rows per copy instruction).  Two LDS stages of 64 KB, the whole
+// 128 KB: the copies of step t + 1 fill the stage step t - 1 read and are
+// issued from the barrier that ends step t - 1 through the first half of
+// step t, one per MFMA; the wait at the end of step t takes all of them.
+//
+// LDS layout: rows of 128 bytes, eight 16-byte chunks, chunk c of row r at
+// position c ^ ((r / 2) % 8).  A fragment read (32 x 32 x 64: lane l takes
+// row l % 32, bytes 64 s + 32 (l / 32) .. + 31 of the step, s the half step)
+// is two 16-byte reads; the 16 lanes of a group read 16 rows at one logical
+// chunk, two rows per 256-byte bank line, and the key puts them on 16
+// different 16-byte slots; lanes l and l + 16 read the same chunk 16 rows
+// apart (same slot, 2 KB apart), which gfx950 serves at full rate.  A copy
+// instruction fills 8 rows: lane p takes physical chunk p % 8 of row p / 8.
+//
+// Schedule of step t (fragment buffer 0 for half step 0, buffer 1 for half
+// step 1): the last 8 MFMAs of step t - 1 with the reads of the six
+// fragment pairs step t's first 8 MFMAs use; the 16 MFMAs of half step 0
+// with the last two pairs of half step 0 and the eight of half step 1; the
+// first 8 MFMAs of half step 1; the wait and the barrier.  The 16 copies of
+// step t + 1 go out one per MFMA from the start of the step.  Copies past
+// the last step are issued with every lane out of range (they write zeros
+// into a stage nobody reads), so the loop has no branch around them.
+template <bool KTAIL, int FMT>
+__global__ __launch_bounds__(256, 1) void fp8_wide_kernel(int M, int N, int K, float alpha,
+                                                          float beta,
+                                                          const uint8_t *__restrict__ A,
+                                                          const uint8_t *__restrict__ B, float *C,
+                                                          int tiles_m, int tiles_n,
+                                                          PPSplit split_plan) {
+    typedef int v8i __attribute__((ext_vector_type(8)));
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+    constexpr int BM = 256, BN = 256, S = 2, BK = kFp8WideBK;  // BK in elements = bytes
+    constexpr int WM = 128, WN = 128, MI = 4, NI = 4;
+    constexpr int STAGE = BM * BK;                   // bytes, A and B alike
+    constexpr int LOADS = BM / 8 / 4;                // 1 KB copies per wave per operand
+    constexpr int COPIES = 2 * LOADS;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[S][STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[S][STAGE];
+
+    int v, split;
+    __shared__ int s_words[2];
+    split_tile(blockIdx.x, split_plan, v, split, &s_words[0]);
+    int tm, tn;
+    grouped_tile(v, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int total_steps = (K + BK - 1) / BK;
+    const int t_begin = split == 1 ? split_plan.split_step : 0;
+    const int t_end = split == 0 ? split_plan.split_step : total_steps;
+    const int T = t_end - t_begin;  // this workgroup's steps; t below counts them
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // copies: lane p of a wave writes physical chunk p % 8 of row 8 wave +
+    // p / 8 (+ 32 q), holding logical chunk (p % 8) ^ ((row / 2) % 8)
+    const int row_in = lane >> 3;
+    const int chunk = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+    const uint32_t off0 = static_cast<uint32_t>((8 * wave + row_in) * K + 16 * chunk);
+    const uint32_t step32 = static_cast<uint32_t>(32 * K);
+    struct StepCopy {
+        i32x4 ra, rb;
+        uint32_t la, lb;
+        bool ok;
+    };
+    auto step_copy = [&](int t) {  // t may be T: then every lane is out of range
+        const int k0 = (t_begin + t) * BK, stage = t % S;
+        StepCopy c;
+        c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                         static_cast<long long>(M - m0) * K - k0);
+        c.rb = make_desc(B + static_cast<size_t>(n0) * K + k0,
+                         static_cast<long long>(N - n0) * K - k0);
+        c.ok = t < T && !(KTAIL && k0 + 16 * chunk >= K);
+        c.la = lds_address(&lds_a[stage][wave * 1024]);
+        c.lb = lds_address(&lds_b[stage][wave * 1024]);
+        return c;
+    };
+    auto issue_copy = [&](const StepCopy &c, int q) {
+        const int r = q % LOADS;
+        if (q < LOADS)
+            lds_dma16(c.ra, c.la + r * 4096, c.ok ? off0 + r * step32 : kOOB);
+        else
+            lds_dma16(c.rb, c.lb + r * 4096, c.ok ? off0 + r * step32 : kOOB);
+    };
+    // L2 warm-up: in step t, right after its last copy, every wave loads
+    // one 4-byte word from each of its 64 rows of A and of B at step t + 2's
+    // k into a scratch LDS area, so that the copies of step t + 2, issued a
+    // step later, find their lines in L2 (those copies otherwise wait on
+    // HBM at the end of their step).  The step's closing wait leaves these
+    // two loads in flight (the counter retires in issue order and they are
+    // the last two).  Rows past M or N and k past K are outside the
+    // descriptors (no access).
+    __shared__ __attribute__((aligned(16))) uint8_t lds_warm[1024];
+    const uint32_t warm_lds = lds_address(&lds_warm[0]);
+    const uint32_t warm_row = static_cast<uint32_t>((64 * wave + lane) * K);
+    auto warm_up = [&](int t) {
+        const int k0 = (t_begin + t) * BK;
+        const i32x4 da = make_desc(A + static_cast<size_t>(m0) * K + k0,
+                                   static_cast<long long>(M - m0) * K - k0);
+        const i32x4 db = make_desc(B + static_cast<size_t>(n0) * K + k0,
+                                   static_cast<long long>(N - n0) * K - k0);
+        const bool ok = t < T;
+        lds_dma4_warm(da, warm_lds, ok ? warm_row : kOOB);
+        lds_dma4_warm(db, warm_lds, ok ? warm_row : kOOB);
+    };
+
+    // fragment reads: half step s, lane half h, read e of a pair takes
+    // logical chunk 4 s + 2 h + e
+    const int swz = (l32 >> 1) & 7;
+    u32x8 fa[2][MI], fb[2][NI];
+    auto load16 = [&](const uint8_t *row_base, int s, int e) {
+        return *reinterpret_cast<const u32x4 *>(row_base + ((4 * s + 2 * h + e) ^ swz) * 16);
+    };
+    // fragment pair `o` (0 .. 7) of half step s into buffer s: B block 0, A
+    // blocks 0 .. 3, B blocks 1 .. 3 (the first eight MFMAs use B blocks 0
+    // and 1)
+    auto read_pair = [&](int stage, int s, int o) {
+        if (o >= 1 && o <= MI) {
+            const int i = o - 1;
+            const uint8_t *rb = &lds_a[stage][(wm * WM + 32 * i + l32) * BK];
+            fa[s][i].lo = load16(rb, s, 0);
+            fa[s][i].hi = load16(rb, s, 1);
+        } else {
+            const int jj = o == 0 ? 0 : o - MI;
+            const uint8_t *rb = &lds_b[stage][(wn * WN + 32 * jj + l32) * BK];
+            fb[s][jj].lo = load16(rb, s, 0);
+            fb[s][jj].hi = load16(rb, s, 1);
+        }
+    };
+    constexpr int kPairs = MI + NI;
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+    auto mfma = [&](int q, int s) {  // B-major: consecutive MFMAs share B
+        const int jj = q / MI, i = q % MI;
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            __builtin_bit_cast(v8i, fb[s][jj]), __builtin_bit_cast(v8i, fa[s][i]), acc[i][jj], FMT,
+            FMT, 0, 127, 0, 127);
+    };
+    constexpr int kMfma = MI * NI;  // per half step
+    constexpr int kTail = 8, kEarly = kMfma - kTail;
+    constexpr int kFirstReads = kPairs - 2;  // what the first 8 MFMAs of a half step use
+    static_assert(COPIES <= kTail + kMfma, "the copies go out before half step 1");
+    constexpr int kWaitWarm = wait_vm(2) & ~(15 << 8);  // vmcnt(2), lgkmcnt(0)
+
+    if (T > 0) {
+        const StepCopy c = step_copy(0);
+#pragma unroll
+        for (int q = 0; q < COPIES; ++q) issue_copy(c, q);
+    }
+    __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0), lgkmcnt(0)
+    __syncthreads();
+
+    // FIRST: step 0, whose first fragments have no previous MFMAs to hide
+    // under and which issues all 16 copies of step 1 in its half step 0
+    auto k_step = [&](int t, auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        const int cur = t % S;
+        const StepCopy next = step_copy(t + 1);
+        // MFMA slot u = 0 .. 23 of the window from the barrier to the end of
+        // half step 0 (the tail, then half step 0) issues copy
+        // copy_at(u): two copies per three slots; step 0, with no tail, one
+        // per slot of half step 0
+        auto copy_at = [](int u) { return FIRST ? u - kTail : (u % 3 == 2 ? -1 : u - u / 3); };
+        if constexpr (!FIRST) {
+#pragma unroll
+            for (int q = 0; q < kTail; ++q) {
+                mfma(kEarly + q, 1);
+                if (q < kFirstReads) read_pair(cur, 0, q);
+                if (copy_at(q) >= 0) issue_copy(next, copy_at(q));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kFirstReads; ++q) read_pair(cur, 0, q);
+        }
+#pragma unroll
+        for (int q = 0; q < kMfma; ++q) {
+            mfma(q, 0);
+            if (q < 2) read_pair(cur, 0, kFirstReads + q);
+            else if (q < 2 + kPairs) read_pair(cur, 1, q - 2);
+            const int cq = copy_at(kTail + q);
+            if (cq >= 0 && cq < COPIES) issue_copy(next, cq);
+            if (cq == COPIES - 1) warm_up(t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int q = 0; q < kEarly; ++q) {
+            mfma(q, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // this wave's copies of step t + 1 and its reads (the two warm-up
+        // loads may stay in flight)
+        __builtin_amdgcn_s_waitcnt(kWaitWarm);
+        __syncthreads();
+    };
+    if (T > 0) k_step(0, std::true_type());
+    for (int t = 1; t < T; ++t) k_step(t, std::false_type());
+    __builtin_amdgcn_s_waitcnt(7 << 4);  // the last warm-up loads
+    if (T > 0) {
+#pragma unroll
+        for (int q = 0; q < kTail; ++q) {
+            mfma(kEarly + q, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // epilogue: as the bf16 kernel's, each wave staging through a private
+    // 16 KB slice of the A stages (the last barrier ended every read, and
+    // the last step's copies were all out of range)
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(C + static_cast<size_t>(m0) * N + n0,
+                  (static_cast<long long>(M - m0) * N - n0) * 4);
+    static_assert(S * STAGE >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
+    float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
+    store_split_tile<MI, false>(acc, region, rc, wm * WM, wn * WN, N - n0, N, alpha, beta, split,
+                                v, split_plan, nullptr, kActNone, &s_words[1]);
+}
+
 // Calls f(ktail, epi) with the two flags as std::integral_constant values, so
 // that a launcher can pick one of its four kernel instantiations.
 template <class F>
@@ -2065,20 +2294,27 @@ int bf16_pick_tile_config(int M, int N, int K, int num_cus, bool allow_split) {
 
 hipError_t launch_fp8_gemm(int M, int N, int K, float alpha, float beta, const uint8_t *A,
                            const uint8_t *B, float *C, int fmt, const PPSplit *split,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool wide) {
     const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const long long tiles = tiles_m * tiles_n;
     if (tiles > 0x3fffffffLL || (fmt != 0 && fmt != 1) || K % 16 != 0)
         return hipErrorInvalidValue;
+    const int bk = wide ? kFp8WideBK : kFp8BK;
     PPSplit plan;
-    if (!make_plan(split, tiles, K, plan, kFp8BK)) return hipErrorInvalidValue;
+    if (!make_plan(split, tiles, K, plan, bk)) return hipErrorInvalidValue;
     const long long grid = plan.split_from + 2 * (tiles - plan.split_from);
     const dim3 g(static_cast<unsigned>(grid)), block(kThreads);
-    const bool ktail = K % kFp8BK != 0;
+    const bool ktail = K % bk != 0;
     const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
     auto go = [&](auto kt, auto f) {
-        fp8_q4_kernel<decltype(kt)::value, decltype(f)::value>
-            <<<g, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn, plan);
+        constexpr bool KT = decltype(kt)::value;
+        constexpr int F = decltype(f)::value;
+        if (wide)
+            fp8_wide_kernel<KT, F><<<g, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn,
+                                                            plan);
+        else
+            fp8_q4_kernel<KT, F><<<g, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn,
+                                                          plan);
     };
     using F0 = std::integral_constant<int, 0>;
     using F1 = std::integral_constant<int, 1>;
@@ -2092,13 +2328,13 @@ hipError_t launch_fp8_gemm(int M, int N, int K, float alpha, float beta, const u
     return hipGetLastError();
 }
 
-int fp8_split_tiles(int M, int N, int K, int num_cus) {
+int fp8_split_tiles(int M, int N, int K, int num_cus, int bk) {
     // as for bf16: split the last round when it is at most half full and
-    // each half keeps at least four 64-deep K steps
+    // each half keeps at least four K steps
     const long long tiles =
         static_cast<long long>((M + kPPTile - 1) / kPPTile) * ((N + kPPTile - 1) / kPPTile);
     const long long r = num_cus > 0 ? tiles % num_cus : 0;
-    const int steps = (K + kFp8BK - 1) / kFp8BK;
+    const int steps = (K + bk - 1) / bk;
     if (r == 0 || 2 * r > num_cus || steps < 8) return 0;
     return static_cast<int>(r);
 }

@@ -160,6 +160,24 @@ __device__ __forceinline__ void lds_dma16(i32x4 desc, uint32_t lds_addr, uint32_
         : "memory");
 }
 
+// An L2 warm-up load with no register destination: 4 bytes per lane from
+// byte offset `voff` of `desc` into LDS at `lds_addr` + 4 * lane (a scratch
+// area nothing reads).  Without sc0 the line is kept in L2 for the copy
+// that follows it; like lds_dma16 it is waited for only through the
+// vector-memory counter, never by the compiler.
+__device__ __forceinline__ void lds_dma4_warm(i32x4 desc, uint32_t lds_addr, uint32_t voff) {
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(desc)
+        : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void *)p));
 }

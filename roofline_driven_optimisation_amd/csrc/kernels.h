@@ -117,15 +117,17 @@ hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float 
                                bool trans_b, hipStream_t stream);
 // 8-bit float GEMM, C = alpha A B^T + beta C with B stored N x K: fmt 0
 // E4M3, 1 E5M2 (both operands).  Needs K % 16 == 0, 16-byte aligned A and
-// B, K <= 2^21 and N <= 2^20.  `split` (or null) splits tiles as for the
-// bf16 256 x 256 kernels, with split_step counted in 64-deep K steps.
-constexpr int kFp8BK = 64;  // bytes (= elements) per K step
+// B, K <= 2^21 and N <= 2^20.  `wide`: the 128-deep K step kernel, else the
+// 64-deep one.  `split` (or null) splits tiles as for the bf16 256 x 256
+// kernels, with split_step counted in the kernel's K steps.
+constexpr int kFp8BK = 64;        // bytes (= elements) per K step
+constexpr int kFp8WideBK = 128;   // the same for the 128-deep kernel
 hipError_t launch_fp8_gemm(int M, int N, int K, float alpha, float beta, const uint8_t *A,
                            const uint8_t *B, float *C, int fmt, const PPSplit *split,
-                           hipStream_t stream);
+                           hipStream_t stream, bool wide);
 // Tiles of an fp8 GEMM worth splitting over K (its last round when at most
-// half full and K has at least 8 steps), else 0.
-int fp8_split_tiles(int M, int N, int K, int num_cus);
+// half full and K has at least 8 steps of `bk`), else 0.
+int fp8_split_tiles(int M, int N, int K, int num_cus, int bk);
 // One thread per output element for any 8-bit float shape or alignment.
 hipError_t launch_naive_fp8(int M, int N, int K, float alpha, float beta, const uint8_t *A,
                             const uint8_t *B, float *C, int fmt, hipStream_t stream);

@@ -195,7 +195,8 @@ def mfma_rows(path: str, last: int = 0):
     return rows
 
 
-def counter_runs(paths, labels, last: int = 8, kernels=("bf16_q4", "bf16_q16", "fp8_q4")):
+def counter_runs(paths, labels, last: int = 8,
+                 kernels=("bf16_q4", "bf16_q16", "fp8_q4", "fp8_wide")):
     """Median counter values per workload from one or more --pmc passes of
     the same bench command: each pass's dispatches are split into runs of
     consecutive dispatches of one kernel and launch shape (one run per

@@ -1,6 +1,8 @@
 """GPU parity of the 8-bit float GEMM (E4M3 and E5M2, B stored N x K, fp32
-C) through the C ABI, against the oracle: the matrix-core kernel (full K
-steps and a K tail, ragged M and N, per-tensor scales, beta), the
+C) through the C ABI, against the oracle: both matrix-core kernels (the
+128-deep K step one the library picks, and the 64-deep one
+MGEMM_FP8_KERNEL selects: full K steps and a K tail, ragged M and N,
+per-tensor scales, beta, split last rounds), the
 one-thread-per-output fallback (K not a multiple of 16, unaligned operands),
 K = 0, exact on integer inputs, within a tolerance derived from each
 kernel's fp32 rounding chain (fp8_tol) on random inputs and on every finite
@@ -20,6 +22,33 @@ pytestmark = pytest.mark.gpu
 
 FMTS = [0, 1]
 FMT_ID = ["e4m3", "e5m2"]
+KERNELS = ["fp8_q4_256x256x128", "fp8_q4_256x256x64"]  # the first is the default
+
+
+@pytest.fixture(params=KERNELS)
+def kernel(request, monkeypatch):
+    """The matrix-core kernel under test (the 64-deep one by MGEMM_FP8_KERNEL)."""
+    if request.param == KERNELS[0]:
+        monkeypatch.delenv("MGEMM_FP8_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("MGEMM_FP8_KERNEL", request.param)
+    return request.param
+
+
+def expected(M, N, K, offset, kernel):
+    """The kernel name gemm_fp8 reports: the one-thread-per-output kernel
+    for K % 16 != 0 or unaligned operands, else the matrix-core kernel,
+    with its last round split over K when that round is at most half full
+    on 256 CUs and K has at least 8 of the kernel's steps (pairs on one XCD
+    when the split tiles are a multiple of 8)."""
+    if K % 16 or offset:
+        return "naive_fp8"
+    tiles = -(-M // 256) * -(-N // 256)
+    r = tiles % 256
+    steps = -(-K // int(kernel.rsplit("x", 1)[1]))
+    if r and 2 * r <= 256 and steps >= 8:
+        return kernel + ("_splitk_xcd" if r % 8 == 0 else "_splitk")
+    return kernel
 
 def fp8_tol(K, kernel):
     """Bound on max |C - C_ref| / den for the 8-bit float GEMM, from the
@@ -85,17 +114,18 @@ def run(A, B, C, alpha, beta, sa, sb, fmt, offset=0):
     return Ct.cpu().numpy(), name
 
 
-CASES = [  # (M, N, K, offset, expected kernel)
-    (256, 256, 64, 0, "fp8_q4_256x256x64"),
-    (300, 520, 256, 0, "fp8_q4_256x256x64"),
-    (300, 520, 144, 0, "fp8_q4_256x256x64"),      # K tail of 16
-    (520, 300, 1072, 0, "fp8_q4_256x256x64_splitk"),      # K tail of 48, split pairs
-    (37, 600, 16, 0, "fp8_q4_256x256x64"),               # one partial K step
-    (1, 1000, 512, 0, "fp8_q4_256x256x64_splitk"),
-    (1024, 512, 1024, 0, "fp8_q4_256x256x64_splitk_xcd"),  # 8 split tiles: pairs on one XCD
-    (1040, 520, 1104, 0, "fp8_q4_256x256x64_splitk"),     # 15 split tiles, K tail of 16
-    (70, 90, 60, 0, "naive_fp8"),                 # K % 16 != 0
-    (70, 90, 64, 1, "naive_fp8"),                 # unaligned A and B
+CASES = [  # (M, N, K, offset)
+    (256, 256, 64, 0),
+    (300, 520, 256, 0),
+    (300, 520, 144, 0),      # K tail of 16 (64-deep), of 16 after one step (128-deep)
+    (520, 300, 1072, 0),     # K tail of 48, split pairs
+    (37, 600, 16, 0),        # one partial K step
+    (1, 1000, 512, 0),       # split by the 64-deep kernel, 4 steps for the 128-deep
+    (1024, 512, 1024, 0),    # 8 split tiles: pairs on one XCD
+    (1040, 520, 1104, 0),    # 15 split tiles, K tail of 16 (64-deep) or 80 (128-deep)
+    (300, 520, 1936, 0),     # 16 steps of 128 less a 16-deep tail
+    (70, 90, 60, 0),         # K % 16 != 0
+    (70, 90, 64, 1),         # unaligned A and B
 ]
 
 
@@ -105,8 +135,9 @@ def ids(c):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
 @pytest.mark.parametrize("case", CASES, ids=ids)
-def test_fp8_exact_integers(case, fmt):
-    M, N, K, offset, want = case
+def test_fp8_exact_integers(case, fmt, kernel):
+    M, N, K, offset = case
+    want = expected(M, N, K, offset, kernel)
     A, B, rng = draw(M, N, K, fmt, "int", seed=M + N + K)
     C = rng.integers(-8, 9, size=(M, N)).astype(np.float32)
     got, name = run(A, B, C, 1.0, 0.5, 1.0, 2.0, fmt, offset)
@@ -117,8 +148,9 @@ def test_fp8_exact_integers(case, fmt):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
 @pytest.mark.parametrize("case", CASES, ids=ids)
-def test_fp8_random(case, fmt):
-    M, N, K, offset, want = case
+def test_fp8_random(case, fmt, kernel):
+    M, N, K, offset = case
+    want = expected(M, N, K, offset, kernel)
     A, B, _ = draw(M, N, K, fmt, "n", seed=7 + K)
     got, name = run(A, B, None, 1.25, 0.0, 0.5, 0.125, fmt, offset)
     assert name == want, name
@@ -130,13 +162,13 @@ def test_fp8_random(case, fmt):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
 @pytest.mark.parametrize("offset", [0, 1], ids=["mfma", "naive"])
-def test_fp8_every_finite_code(fmt, offset):
+def test_fp8_every_finite_code(fmt, offset, kernel):
     """Operands drawn from every finite code of the format: subnormals,
     both zeros' neighbours and the largest magnitudes (448 and 57344)."""
     M, N, K = 264, 288, 320
     A, B, _ = draw(M, N, K, fmt, "codes", seed=11 + fmt)
     got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt, offset)
-    assert name == ("naive_fp8" if offset else "fp8_q4_256x256x64"), name
+    assert name == ("naive_fp8" if offset else kernel), name
     ref, den = oracle.gemm_fp8(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
     err = oracle.parity_error(got, ref, den)
     log("  fp8 all-codes err=%.3e tol=%.2e" % (err, fp8_tol(K, name)))
@@ -144,7 +176,7 @@ def test_fp8_every_finite_code(fmt, offset):
 
 
 @pytest.mark.parametrize("shape", [(520, 300, 1072), (1024, 512, 1024)], ids=["pairs", "xcd"])
-def test_fp8_split_repeats(shape):
+def test_fp8_split_repeats(shape, kernel):
     """Split tiles exchange partials through flags with a fresh epoch per
     call: three calls in a row give the same bits, equal to the oracle on
     integers."""
@@ -154,12 +186,12 @@ def test_fp8_split_repeats(shape):
     ref, _ = oracle.gemm_fp8(A, B, C, 1.0, 0.5, 1.0, 1.0, 0)
     for _ in range(3):
         got, name = run(A, B, C, 1.0, 0.5, 1.0, 1.0, 0)
-        assert "splitk" in name, name
+        assert name == expected(M, N, K, 0, kernel) and "splitk" in name, name
         assert np.array_equal(got.astype(np.float64), ref)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
-def test_fp8_instruction_grouping(fmt):
+def test_fp8_instruction_grouping(fmt, kernel):
     """The summation the matrix-core kernel's tolerance rests on, seen
     through gemm_fp8 on one output (M = N = 1, K = 64: one instruction; B
     stored N x K, so column 0 of B is its row 0): with a product 1 at k =
@@ -176,7 +208,7 @@ def test_fp8_instruction_grouping(fmt):
             a[0, k], b[0, k] = x, y
         A, B = f32_to_fp8_bits(a, fmt), f32_to_fp8_bits(b, fmt)
         got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
-        assert name == "fp8_q4_256x256x64", name
+        assert name == kernel, name
         return float(got[0, 0])
 
     h13, h14 = 2.0 ** -7, 2.0 ** -7  # 2^-13 = 2^-7 * 2^-6, 2^-14 = 2^-7 * 2^-7
@@ -187,7 +219,7 @@ def test_fp8_instruction_grouping(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
-def test_fp8_positive_operands(fmt):
+def test_fp8_positive_operands(fmt, kernel):
     """Positive operands make |C| equal to den, so the tolerance also
     bounds the error relative to C itself: an output rounded to a 16-bit
     type (2^-9 relative) would fail here."""
@@ -196,6 +228,7 @@ def test_fp8_positive_operands(fmt):
     A = f32_to_fp8_bits(np.abs(rng.standard_normal((M, K))).astype(np.float32), fmt)
     B = f32_to_fp8_bits(np.abs(rng.standard_normal((N, K)) * 0.5).astype(np.float32), fmt)
     got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
+    assert name == expected(M, N, K, 0, kernel), name
     ref, den = oracle.gemm_fp8(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
     err = oracle.parity_error(got, ref, den)
     log("  fp8 positive err=%.3e tol=%.2e (2^-9 = %.2e)" % (err, fp8_tol(K, name), 2.0 ** -9))
@@ -211,19 +244,20 @@ def test_fp8_k_zero():
     assert np.array_equal(got, C * 0.5)
 
 
-FULL = [(4096, 4096, 4096, "fp8_q4_256x256x64"),
-        (2048, 11008, 4096, "fp8_q4_256x256x64_splitk_xcd")]
+FULL = [(4096, 4096, 4096), (2048, 11008, 4096)]
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
 @pytest.mark.parametrize("shape", FULL, ids=lambda c: "%dx%dx%d" % c[:3])
 def test_fp8_full_size(shape, fmt):
     """The sizes the throughput is measured at (4096^3; 2048 x 11008 x 4096,
-    whose third-full last round is split over K) against the oracle: the
-    whole output for E4M3, the format the benchmark runs, and the 256
-    leading and 256 trailing rows for E5M2 (the oracle decodes every byte
-    in its inner loop and takes over a minute per full product)."""
-    M, N, K, want = shape
+    whose third-full last round is split over K), with the kernel the
+    library picks, against the oracle: the whole output for E4M3, the
+    format the benchmark runs, and the 256 leading and 256 trailing rows
+    for E5M2 (the oracle decodes every byte in its inner loop and takes
+    over a minute per full product)."""
+    M, N, K = shape
+    want = expected(M, N, K, 0, KERNELS[0])
     A, B, rng = draw(M, N, K, fmt, "n", seed=5)
     got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
     assert name == want, name
@@ -237,13 +271,14 @@ def test_fp8_full_size(shape, fmt):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_ID)
 @pytest.mark.parametrize("shape", FULL, ids=lambda c: "%dx%dx%d" % c[:3])
-def test_fp8_full_size_integers(shape, fmt):
+def test_fp8_full_size_integers(shape, fmt, kernel):
     """The benchmarked sizes with integer entries in [-4, 4] (exact in both
     formats; every product, group sum and partial sum is an integer below
-    2^24, so exact in fp32 whatever the summation): the whole output must
-    equal the product of the oracle's decoded operands, element for
-    element, split tiles included."""
-    M, N, K, want = shape
+    2^24, so exact in fp32 whatever the summation), on both kernels: the
+    whole output must equal the product of the oracle's decoded operands,
+    element for element, split tiles included."""
+    M, N, K = shape
+    want = expected(M, N, K, 0, kernel)
     A, B, _ = draw(M, N, K, fmt, "int", seed=8)
     got, name = run(A, B, None, 1.0, 0.0, 1.0, 1.0, fmt)
     assert name == want, name

@@ -104,7 +104,7 @@ def test_fp8_split_shape_unsplit_under_capture(torch):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         binding.gemm_fp8(A, B, C, 1.0, 0.5)
-    assert binding.last_kernel() == "fp8_q4_256x256x64", binding.last_kernel()
+    assert binding.last_kernel() == "fp8_q4_256x256x128", binding.last_kernel()
     for r in range(4):
         C.copy_(C0)
         g.replay()

@@ -93,7 +93,7 @@ def test_fp8_split_wait_timeout_is_reported(gpu):
         binding.set_test_hook(binding.TEST_POLL_LIMIT, 0)
         Ct = torch.zeros(M, N, device="cuda")
         binding.gemm_fp8(At, Bt, Ct, 1.0, 0.0)
-        assert binding.last_kernel() == "fp8_q4_256x256x64_splitk"
+        assert binding.last_kernel() == "fp8_q4_256x256x128_splitk"
         assert binding.split_timeouts() == 6
         assert bool(torch.isnan(Ct).all())
     finally:
