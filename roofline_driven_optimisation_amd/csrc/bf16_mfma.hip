@@ -83,6 +83,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;
 
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima).
+constexpr int wait_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int BM, int BN>
@@ -687,10 +692,6 @@ struct PPTile {
 
 __device__ __forceinline__ int swz_a32(int r) { return (r >> 2) & 3; }
 
-// s_waitcnt immediate that waits until at most `vm` vector-memory operations
-// are outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 and
-// lgkmcnt 11:8 left at their maxima).
-constexpr int wait_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
 
 // ---- the split pair's handshake (see PPSplit) ------------------------------
 // LOCAL pairs share one XCD and exchange through ordinary memory whose

@@ -29,11 +29,13 @@ KERNEL_SOURCES = {
     "bf16_mfma": "bf16_mfma.hip",
     "bf16_pp": "bf16_mfma.hip",
     "bf16_q4": "bf16_mfma.hip",
+    "bf16_q16": "bf16_mfma.hip",
     "f32_mfma": "f32_mfma.hip",
     "f32_dma": "f32_mfma.hip",
     "skinny": "skinny_bf16.hip",
     "naive": "naive.hip",
     "fp8_q4": "bf16_mfma.hip",
+    "fp8_wide": "bf16_mfma.hip",
     "reduce": "reduce.hip",
 }
 
