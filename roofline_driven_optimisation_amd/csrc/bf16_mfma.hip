@@ -427,7 +427,12 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
                                                cols_left, N, alpha, beta, rw, ldw, bias, act);
 }
 
-template <int BM, int BN, bool KTAIL, bool EPI>
+// TRANSB: B is stored N x K (row n holds B[.][n] along k, as attention's
+// K): its tile (BN rows n, 64 k) is copied, laid out and read exactly like
+// A's.  STAGED (128 x 128 only): the epilogue goes through LDS
+// (store_c_tile_lds, whole 256-byte row segments per store) instead of
+// 16-byte stores straight from the accumulators.
+template <int BM, int BN, bool KTAIL, bool EPI, bool TRANSB = false, bool STAGED = false>
 __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, int K, float alpha,
                                                                 float beta,
                                                                 const uint16_t *__restrict__ A,
@@ -487,13 +492,18 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
         uint32_t la, lb;
         bool a_ok;
     };
+    static_assert(!TRANSB || T::B_LOADS == BN / 32, "a transposed B tile copies like A's");
     auto tile_copy = [&](int k0, int stage) {
         TileCopy c;
         // descriptors based at the tile origin
         c.ra = make_desc(A + static_cast<size_t>(m0) * K + k0,
                          (static_cast<long long>(M - m0) * K - k0) * 2);
-        c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
-                         (static_cast<long long>(K - k0) * N - n0) * 2);
+        if constexpr (TRANSB)
+            c.rb = make_desc(B + static_cast<size_t>(n0) * K + k0,
+                             (static_cast<long long>(N - n0) * K - k0) * 2);
+        else
+            c.rb = make_desc(B + static_cast<size_t>(k0) * N + n0,
+                             (static_cast<long long>(K - k0) * N - n0) * 2);
         c.a_ok = !(KTAIL && k0 + 8 * a_chunk >= K);
         c.la = lds_address(&lds_a[stage][wave * 512]);
         c.lb = lds_address(&lds_b[stage][wave * 512]);
@@ -502,6 +512,9 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     auto issue_copy = [&](const TileCopy &c, int q) {
         if (q < T::A_LOADS)
             lds_dma16(c.ra, c.la + q * 4 * 1024, c.a_ok ? a_off + q * a_step : kOOB);
+        else if constexpr (TRANSB)
+            lds_dma16(c.rb, c.lb + (q - T::A_LOADS) * 4 * 1024,
+                      c.a_ok ? a_off + (q - T::A_LOADS) * a_step : kOOB);
         else
             lds_dma16(c.rb, c.lb + (q - T::A_LOADS) * 4 * 1024,
                       b_ok ? b_off + (q - T::A_LOADS) * b_step : kOOB);
@@ -523,8 +536,10 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     const int b_row_lane = 8 * (g >> 1) + (j16 >> 2);                  // + 16 s + 4 r
 
     // Fragment read number q of k16 sub-step s: q < MI reads A block q, the
-    // rest read half (q - MI) % 2 of B block (q - MI) / 2.
-    constexpr int kReads = T::MI + 2 * T::NI;
+    // rest read half (q - MI) % 2 of B block (q - MI) / 2 (TRANSB: all of B
+    // block q - MI, read like an A block).
+    constexpr int kReads = T::MI + (TRANSB ? 1 : 2) * T::NI;
+    const int bt_lane_base = (wn * T::WN + l32) * kBK;
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     auto read_one = [&](int stage, int s, int q, bf16x8 (&a)[T::MI], s16x8 (&b)[T::NI]) {
         if (q < T::MI) {
@@ -532,6 +547,11 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
             const u32x4 v = *reinterpret_cast<const u32x4 *>(
                 &lds_a[stage][a_lane_base + 32 * q * kBK + pos]);
             a[q] = __builtin_bit_cast(bf16x8, v);
+        } else if constexpr (TRANSB) {
+            const int pos = ((2 * s + h) ^ swz_a(l32)) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                &lds_b[stage][bt_lane_base + 32 * (q - T::MI) * kBK + pos]);
+            b[q - T::MI] = __builtin_bit_cast(s16x8, v);
         } else {
             const int jj = (q - T::MI) >> 1, r = (q - T::MI) & 1;
             const int row = 16 * s + 4 * r + b_row_lane;
@@ -632,8 +652,19 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
-    store_c_tile<T::MI, T::NI, EPI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta,
-                                    epi.bias ? epi.bias + n0 : nullptr, epi.act);
+    if constexpr (STAGED) {
+        // every wave's last reads are done before any wave reuses a stage:
+        // waves 0 and 1 stage through the two A stages, 2 and 3 the B stages
+        static_assert(BM == 128 && BN == 128, "16 KB stages, one per wave");
+        __syncthreads();
+        float *region = reinterpret_cast<float *>(wave < 2 ? &lds_a[wave][0] : &lds_b[wave - 2][0]);
+        store_c_tile_lds<T::MI, T::NI, kStoreC, kSystemScope, EPI>(
+            acc, region, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta, rc, 0,
+            EPI && epi.bias ? epi.bias + n0 : nullptr, epi.act);
+    } else {
+        store_c_tile<T::MI, T::NI, EPI>(acc, rc, wm * T::WM, wn * T::WN, N - n0, N, alpha, beta,
+                                        epi.bias ? epi.bias + n0 : nullptr, epi.act);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2204,15 +2235,38 @@ hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_
 template <int BM, int BN>
 hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                       const uint16_t *B, float *C, const Epi &epi, hipStream_t stream,
-                      const Batch &batch = kOneItem) {
+                      const Batch &batch = kOneItem, bool trans_b = false, bool staged = false) {
     const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long tiles = tiles_m * tiles_n * batch.items;
     if (tiles > 0x7fffffffLL || batch.items < 1) return hipErrorInvalidValue;
+    if ((trans_b || staged) && (epi_on(epi) || BM != 128 || BN != 128))
+        return hipErrorInvalidValue;  // batched 128 x 128 calls only
+    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+    if constexpr (BM == 128 && BN == 128) {
+        if (trans_b || staged) {
+            auto go = [&](auto kt, auto tb, auto st) {
+                bf16_mfma_kernel<BM, BN, decltype(kt)::value, false, decltype(tb)::value,
+                                 decltype(st)::value>
+                    <<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn, epi,
+                                                 batch);
+            };
+            auto with_st = [&](auto kt, auto tb) {
+                if (staged) go(kt, tb, std::true_type());
+                else go(kt, tb, std::false_type());
+            };
+            auto with_tb = [&](auto kt) {
+                if (trans_b) with_st(kt, std::true_type());
+                else with_st(kt, std::false_type());
+            };
+            if (K % kBK != 0) with_tb(std::true_type());
+            else with_tb(std::false_type());
+            return hipGetLastError();
+        }
+    }
     with_flags(K % kBK != 0, epi_on(epi), [&](auto ktail, auto e) {
         bf16_mfma_kernel<BM, BN, decltype(ktail)::value, decltype(e)::value>
-            <<<dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream>>>(
-                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
-                static_cast<int>(tiles_n), epi, batch);
+            <<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn, epi, batch);
     });
     return hipGetLastError();
 }
@@ -2342,7 +2396,7 @@ int fp8_split_tiles(int M, int N, int K, int num_cus, int bk) {
 
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
                                const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
-                               bool trans_b, hipStream_t stream) {
+                               bool trans_b, hipStream_t stream, bool staged) {
     switch (cfg) {
         case 0:
             return launch_q4<false>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
@@ -2351,8 +2405,8 @@ hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float 
             return launch_q4<true>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
                                    trans_b);
         case 3:
-            if (trans_b) return hipErrorInvalidValue;
-            return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, kNoEpi, stream, batch);
+            return launch_cfg<128, 128>(M, N, K, alpha, beta, A, B, C, kNoEpi, stream, batch,
+                                        trans_b, staged);
         default: return hipErrorInvalidValue;
     }
 }

@@ -108,13 +108,14 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
                             const uint16_t *A, const uint16_t *B, float *C, const PPSplit *split,
                             const Epi &epi, hipStream_t stream);
 // Strided batched bf16 GEMM on the tiled kernels, no split and no fused
-// epilogue: `cfg` 0 (the four-wave 256 x 256 kernel, which also takes a B
-// stored transposed, N x K, when trans_b) or 3 (128 x 128, B as K x N).  The
-// same shape requirements as launch_bf16_mfma, for every item (strides keep
-// each item 16-byte aligned).
+// epilogue: `cfg` 0 (the four-wave 256 x 256 kernel), 3 (128 x 128) or 5
+// (the four-wave kernel on 16 x 16 MFMAs), each with B as K x N or stored
+// transposed, N x K (trans_b); `staged` (cfg 3 only) stores C through LDS.
+// The same shape requirements as launch_bf16_mfma, for every item (strides
+// keep each item 16-byte aligned).
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
                                const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
-                               bool trans_b, hipStream_t stream);
+                               bool trans_b, hipStream_t stream, bool staged = false);
 // 8-bit float GEMM, C = alpha A B^T + beta C with B stored N x K: fmt 0
 // E4M3, 1 E5M2 (both operands).  Needs K % 16 == 0, 16-byte aligned A and
 // B, K <= 2^21 and N <= 2^20.  `wide`: the 128-deep K step kernel, else the

@@ -1,10 +1,11 @@
 """GPU parity of the strided batched bf16 GEMM (attention's S = Q K^T with K
 stored token-major, and O = P V) through the C ABI, against the oracle item
 by item: every path (the four-wave 256 x 256 kernel with B as K x N or
-stored transposed, the 128 x 128 kernel for N <= 128, the
-one-thread-per-output fallback), exact on integer inputs, within the bf16 tolerance on random
-ones, and at the attention shapes of a 2048-token, 32-head, d = 128 layer
-over every head's whole output."""
+stored transposed, the 128 x 128 kernel for N <= 128 and, forced, with B
+stored transposed, C through LDS or straight from the accumulators, the
+one-thread-per-output fallback), exact on integer inputs, within the bf16
+tolerance on random ones, and at the attention shapes of a 2048-token,
+32-head, d = 128 layer over every head's whole output."""
 import ctypes
 
 import numpy as np
@@ -61,6 +62,7 @@ CASES = [  # (batch, M, N, K, trans_b, expected kernel)
     (1, 512, 512, 64, True, "bf16_q4_256x256x32_batched_bt"),
     (3, 37, 100, 60, False, "naive_bf16_batched"),
     (3, 37, 100, 60, True, "naive_bf16_batched"),
+    (2, 70, 130, 64, True, "naive_bf16_batched"),                # N % 8 != 0, B transposed
     (2, 40, 72, 0, True, "naive_bf16_batched"),                  # K = 0: beta * C
 ]
 
@@ -86,6 +88,47 @@ def test_batched_random(case):
     assert err <= TOL["bf16"]
 
 
+# the 128 x 128 tile forced (MGEMM_BF16_TILE), B either way, C stored
+# through LDS (the default) or straight from the accumulators
+# (MGEMM_BATCHED_STAGED=0)
+TILE128 = [  # (batch, M, N, K, trans_b)
+    (3, 300, 520, 128, True),
+    (3, 300, 520, 136, True),    # K tail
+    (2, 264, 120, 72, True),     # N < 128, two K steps with a tail
+    (1, 512, 512, 64, True),
+    (3, 300, 520, 136, False),
+    (4, 300, 128, 264, False),
+]
+
+
+def force_128(monkeypatch, staged):
+    monkeypatch.setenv("MGEMM_BF16_TILE", "bf16_mfma_128x128x64")
+    monkeypatch.setenv("MGEMM_BATCHED_STAGED", "1" if staged else "0")
+
+
+def name_128(trans_b, staged):
+    return ("bf16_mfma_128x128x64_batched" + ("_bt" if trans_b else "") +
+            ("" if staged else "_direct"))
+
+
+@pytest.mark.parametrize("staged", [False, True], ids=["direct", "lds"])
+@pytest.mark.parametrize("case", TILE128, ids=lambda c: "%dx%dx%dx%d_%s" % (c[:4] + ("bt" if c[4] else "bn",)))
+def test_batched_128_tile(case, staged, monkeypatch):
+    """Exact on integers (beta 0.5) and within the bf16 tolerance on normal
+    draws."""
+    batch, M, N, K, trans_b = case
+    force_128(monkeypatch, staged)
+    A, B, C = make(batch, M, N, K, trans_b, "i:4", "i:4", 0.5, seed=batch * 100 + K + 1)
+    got, name = run(A, B, C, 1.0, 0.5, trans_b, N)
+    assert name == name_128(trans_b, staged), name
+    ref, _ = oracle.gemm_batched(A, B, C, 1.0, 0.5, bf16=True, trans_b=trans_b)
+    assert np.array_equal(got.astype(np.float64), ref)
+    A, B, _ = make(batch, M, N, K, trans_b, "n:1", "n:0.1", 0.0, seed=8 + K)
+    got, _ = run(A, B, None, 1.25, 0.0, trans_b, N)
+    ref, den = oracle.gemm_batched(A, B, None, 1.25, 0.0, bf16=True, trans_b=trans_b)
+    assert oracle.parity_error(got, ref, den) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("trans_b", [True, False], ids=["qk", "pv"])
 def test_attention_shapes_full(trans_b):
     """32 heads, 2048 tokens, d = 128: S = Q K^T (M = N = 2048, K = 128, K
@@ -107,11 +150,15 @@ def test_attention_shapes_full(trans_b):
     assert worst <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("tile", ["picked", "128_direct", "128_lds"])
 @pytest.mark.parametrize("trans_b", [True, False], ids=["qk", "pv"])
-def test_attention_shapes_integers(trans_b):
+def test_attention_shapes_integers(trans_b, tile, monkeypatch):
     """The same 32-head shapes with integer entries in [-3, 3]: every partial
     sum is an integer below 2^24, so all 32 heads' outputs must equal the
-    exact products bit for bit."""
+    exact products bit for bit (with the tile the library picks, and with
+    the 128 x 128 tile either way of storing C)."""
+    if tile != "picked":
+        force_128(monkeypatch, tile == "128_lds")
     H, T, d = 32, 2048, 128
     M, N, K = (T, T, d) if trans_b else (T, d, T)
     rng = np.random.default_rng(4)
