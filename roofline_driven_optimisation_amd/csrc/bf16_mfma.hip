@@ -1138,11 +1138,11 @@ __device__ __forceinline__ void store_split_tile(const f32x16 (&acc)[MI][4], flo
 // (a K tail) are skipped per step.  The epilogue stages each wave's tile
 // through LDS (store_c_tile_lds128), about 1 % faster than direct 16-byte
 // stores.
-template <bool KTAIL, bool EPI, bool TRANSB>
+template <bool KTAIL, bool EPI, bool TRANSB, bool PERSIST = false>
 __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, float alpha,
                                                          float beta,
-                                                         const uint16_t *__restrict__ A,
-                                                         const uint16_t *__restrict__ B, float *C,
+                                                         const uint16_t *__restrict__ A0,
+                                                         const uint16_t *__restrict__ B0, float *C0,
                                                          int tiles_m, int tiles_n,
                                                          PPSplit split_plan, Epi epi,
                                                          Batch batch) {
@@ -1159,20 +1159,36 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
 
     // Tile and K range: as in the ping-pong kernel, workgroups below
     // split_from own a whole tile (XCD-aware order) and the rest come in
-    // pairs that share a tile, one per half of the K steps.
+    // pairs that share a tile, one per half of the K steps.  PERSIST (a
+    // batched launch, never split, on a grid that is a multiple of 8 and
+    // smaller than the tile count): workgroup b takes the tiles that
+    // workgroups b, b + grid, b + 2 grid, ... would take, all on its XCD.
     int v, split;
     __shared__ int s_words[2];
-    split_tile(blockIdx.x, split_plan, v, split, &s_words[0]);
+    const int per_item = tiles_m * tiles_n;
+    const uint16_t *A, *B;
+    float *C;
+    int m0, n0;
     // A batched launch (never split) numbers the tiles of all items in
     // turn: the XCD-aware order keeps one item's tiles on one XCD.
-    const int per_item = tiles_m * tiles_n;
-    const int item = v / per_item;
-    A += item * batch.stride_a;
-    B += item * batch.stride_b;
-    C += item * batch.stride_c;
-    int tm, tn;
-    grouped_tile(v - item * per_item, tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    auto set_tile = [&](int bid) {
+        if constexpr (PERSIST) {
+            v = xcd_remap(bid, split_plan.grid_tiles);
+            split = -1;
+        } else {
+            split_tile(bid, split_plan, v, split, &s_words[0]);
+        }
+        const int item = v / per_item;
+        A = A0 + item * batch.stride_a;
+        B = B0 + item * batch.stride_b;
+        C = C0 + item * batch.stride_c;
+        int tm, tn;
+        grouped_tile(v - item * per_item, tiles_m, tiles_n, 4, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    };
+    int bid = blockIdx.x;
+    set_tile(bid);
     const int total_steps = (K + BK - 1) / BK;
     const int t_begin = split == 1 ? split_plan.split_step : 0;
     const int t_end = split == 0 ? split_plan.split_step : total_steps;
@@ -1187,7 +1203,7 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     const uint32_t a_step = static_cast<uint32_t>(64 * K * 2);
     const int b_row0 = B_ROWS * wave + lane / B_CHUNKS;
     const int b_c = (lane % B_CHUNKS) ^ swz_b(b_row0);
-    const bool b_ok = (n0 + 8 * b_c) < N;
+    bool b_ok = (n0 + 8 * b_c) < N;
     const uint32_t b_off = static_cast<uint32_t>((b_row0 * N + 8 * b_c) * 2);
     const uint32_t b_step = static_cast<uint32_t>(4 * B_ROWS * N * 2);
 
@@ -1268,12 +1284,15 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     };
 
     f32x16 acc[MI][NI];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < NI; ++jj)
+            for (int jj = 0; jj < NI; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+    };
+    if constexpr (!PERSIST) zero_acc();
     bf16x8 fa[2][MI];
     s16x8 fb[2][NI];
     // MFMA q of a sub-step is block (q % MI, q / MI): consecutive MFMAs
@@ -1291,19 +1310,18 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
     constexpr int kWaitDrain = (7 << 4);
 
     const int T = t_end - t_begin;
-    for (int t = 0; t < S - 1; ++t)
-        if (t < T) {
-            const StepCopy c = step_copy(t);
+    auto issue_step = [&](int t) {
+        const StepCopy c = step_copy(t);
 #pragma unroll
-            for (int q = 0; q < COPIES; ++q) issue_copy(c, q);
-        }
+        for (int q = 0; q < COPIES; ++q) issue_copy(c, q);
+    };
+    for (int t = 0; t < S - 1; ++t)
+        if (t < T) issue_step(t);
     if (T >= S - 1)
         __builtin_amdgcn_s_waitcnt(kWaitSteady);
     else
         __builtin_amdgcn_s_waitcnt(kWaitDrain);
     __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kReads; ++r) read_in_order(0, 0, r, fa[0], fb[0]);
 
     // One K step (stage t % 4): the tail of the previous step's second k16
     // sub-step with this step's first reads; sub-step 0 with the reads of
@@ -1343,27 +1361,77 @@ __global__ __launch_bounds__(256, 1) void bf16_q4_kernel(int M, int N, int K, fl
         __syncthreads();
     };
     const int copy_end = max(0, T - (S - 1));
-    int t = 0;
-    for (; t < copy_end; ++t) k_step(t, std::true_type());
-    for (; t < T; ++t) k_step(t, std::false_type());
+    static_assert(S == 4, "the persistent epilogue takes stage 3 and two more slices");
+    const int total_tiles = split_plan.grid_tiles;
+    for (;;) {
+        if constexpr (PERSIST) zero_acc();
 #pragma unroll
-    for (int q = 0; q < kTail; ++q) {
-        mfma(kEarly + q, 1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int r = 0; r < kReads; ++r) read_in_order(0, 0, r, fa[0], fb[0]);
+        int t = 0;
+        for (; t < copy_end; ++t) k_step(t, std::true_type());
+        for (; t < T; ++t) k_step(t, std::false_type());
+#pragma unroll
+        for (int q = 0; q < kTail; ++q) {
+            mfma(kEarly + q, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
-    // After the last barrier no LDS stage is read and no copy is in flight;
-    // each wave stages its tile through a private 16 KB slice of the A
-    // stages.
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(C + static_cast<size_t>(m0) * N + n0,
-                  (static_cast<long long>(M - m0) * N - n0) * 4);
-    static_assert(S * A_STAGE * 2 >= 4 * 16384, "four 16 KB epilogue slices fit in the A stages");
-    float *region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
-    const int row0 = wm * WM, col0 = wn * WN;
-    const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
-    store_split_tile<MI, EPI>(acc, region, rc, row0, col0, N - n0, N, alpha, beta, split, v,
-                              split_plan, bias, epi.act, &s_words[1]);
+        // After the last barrier no LDS stage is read and no copy is in
+        // flight.  Each wave stages its tile through a private 16 KB LDS
+        // slice: one of the A stages or, with PERSIST, stage 3's A or B
+        // half or one of two more slices (which fill the CU's 160 KB),
+        // while the next tile's first three steps are copied into stages 0
+        // to 2.
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(C + static_cast<size_t>(m0) * N + n0,
+                      (static_cast<long long>(M - m0) * N - n0) * 4);
+        static_assert(S * A_STAGE * 2 >= 4 * 16384,
+                      "four 16 KB epilogue slices fit in the A stages");
+        static_assert(A_STAGE * 2 == 16384 && B_STAGE * 2 == 16384, "16 KB stages");
+        float *region;
+        if constexpr (PERSIST) {
+            __shared__ __attribute__((aligned(16))) float lds_x[2][4096];
+            region = wave == 0   ? reinterpret_cast<float *>(&lds_a[S - 1][0])
+                     : wave == 1 ? reinterpret_cast<float *>(&lds_b[S - 1][0])
+                                 : &lds_x[wave - 2][0];
+        } else {
+            region = reinterpret_cast<float *>(&lds_a[0][0]) + wave * 4096;
+        }
+        const int row0 = wm * WM, col0 = wn * WN;
+        const int tile_n0 = n0, tile_v = v, tile_split = split;
+        const float *bias = EPI && epi.bias ? epi.bias + n0 : nullptr;  // tile's first column
+        bool more = false;
+        if constexpr (PERSIST) {
+            bid += gridDim.x;
+            more = bid < total_tiles;
+            if (more) {
+                set_tile(bid);
+                b_ok = (n0 + 8 * b_c) < N;
+                for (int tt = 0; tt < S - 1; ++tt)
+                    if (tt < T) issue_step(tt);
+            }
+        }
+        if constexpr (PERSIST) {
+            // The epilogue's row offsets are the same for every tile: an
+            // opaque copy of N keeps the compiler from computing them once
+            // before the tile loop and holding them (spilled) through it.
+            int n_ld = N;
+            asm volatile("" : "+s"(n_ld));
+            store_c_tile_lds128<MI, kStoreC, kSystemScope, EPI>(acc, region, rc, row0, col0,
+                                                                n_ld - tile_n0, n_ld, alpha, beta,
+                                                                rc, 0, bias, epi.act);
+        }
+        else
+            store_split_tile<MI, EPI>(acc, region, rc, row0, col0, N - tile_n0, N, alpha, beta,
+                                      tile_split, tile_v, split_plan, bias, epi.act, &s_words[1]);
+        if (!more) break;
+        // Stores and loads share the vector-memory counter and may complete
+        // out of order, so the next tile's first three steps are awaited
+        // with everything else; the barrier also ends every wave's epilogue
+        // reads of stage 3 before step 3's copies overwrite it.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
 }
 
 
@@ -2195,31 +2263,41 @@ bool make_plan(const PPSplit *split, long long tiles, int K, PPSplit &plan, int 
     return true;
 }
 
+// persist_grid > 0 (the 32 x 32 kernel, batched calls only): a persistent
+// grid of that many workgroups, a multiple of 8, when there are more tiles.
 template <bool Q16>
 hipError_t launch_q4(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                      const uint16_t *B, float *C, const PPSplit *split, const Epi &epi,
-                     hipStream_t stream, const Batch &batch = kOneItem, bool trans_b = false) {
+                     hipStream_t stream, const Batch &batch = kOneItem, bool trans_b = false,
+                     int persist_grid = 0) {
     const long long tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const long long tiles = tiles_m * tiles_n;
     const long long total = tiles * batch.items;
     if (total > 0x3fffffffLL || batch.items < 1 || (batch.items > 1 && split != nullptr))
         return hipErrorInvalidValue;
+    if (persist_grid < 0 || persist_grid % 8 != 0 ||
+        (persist_grid > 0 && (Q16 || split || epi_on(epi))))
+        return hipErrorInvalidValue;
     PPSplit plan;
     if (!make_plan(split, total, K, plan)) return hipErrorInvalidValue;
-    const long long grid = plan.split_from + 2 * (total - plan.split_from);
+    const bool persist = persist_grid > 0 && total > persist_grid;
+    const long long grid = persist ? persist_grid : plan.split_from + 2 * (total - plan.split_from);
     auto go = [&](auto ktail, auto e, auto tb) {
         constexpr bool KT = decltype(ktail)::value, EP = decltype(e)::value,
                        TB = decltype(tb)::value;
+        const dim3 g(static_cast<unsigned>(grid));
         if constexpr (Q16)
-            bf16_q16_kernel<KT, EP, TB><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                                          stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                    static_cast<int>(tiles_m),
-                                                    static_cast<int>(tiles_n), plan, epi, batch);
+            bf16_q16_kernel<KT, EP, TB><<<g, dim3(kThreads), 0, stream>>>(
+                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
+                static_cast<int>(tiles_n), plan, epi, batch);
+        else if (!EP && persist)  // batched calls carry no fused epilogue
+            bf16_q4_kernel<KT, false, TB, true><<<g, dim3(kThreads), 0, stream>>>(
+                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
+                static_cast<int>(tiles_n), plan, epi, batch);
         else
-            bf16_q4_kernel<KT, EP, TB><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                                         stream>>>(M, N, K, alpha, beta, A, B, C,
-                                                   static_cast<int>(tiles_m),
-                                                   static_cast<int>(tiles_n), plan, epi, batch);
+            bf16_q4_kernel<KT, EP, TB><<<g, dim3(kThreads), 0, stream>>>(
+                M, N, K, alpha, beta, A, B, C, static_cast<int>(tiles_m),
+                static_cast<int>(tiles_n), plan, epi, batch);
     };
     if (trans_b) {
         if (epi_on(epi)) return hipErrorInvalidValue;  // no fused epilogue in batched calls
@@ -2396,11 +2474,12 @@ int fp8_split_tiles(int M, int N, int K, int num_cus, int bk) {
 
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
                                const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
-                               bool trans_b, hipStream_t stream, bool staged) {
+                               bool trans_b, hipStream_t stream, bool staged, int persist_grid) {
+    if (persist_grid != 0 && cfg != 0) return hipErrorInvalidValue;
     switch (cfg) {
         case 0:
             return launch_q4<false>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
-                                    trans_b);
+                                    trans_b, persist_grid);
         case 5:
             return launch_q4<true>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,
                                    trans_b);

@@ -1,11 +1,13 @@
 """GPU parity of the strided batched bf16 GEMM (attention's S = Q K^T with K
 stored token-major, and O = P V) through the C ABI, against the oracle item
 by item: every path (the four-wave 256 x 256 kernel with B as K x N or
-stored transposed, the 128 x 128 kernel for N <= 128 and, forced, with B
-stored transposed, C through LDS or straight from the accumulators, the
-one-thread-per-output fallback), exact on integer inputs, within the bf16
-tolerance on random ones, and at the attention shapes of a 2048-token,
-32-head, d = 128 layer over every head's whole output."""
+stored transposed, on one workgroup per tile or on a persistent grid when
+there are more tiles than CUs, the 128 x 128 kernel for N <= 128 and,
+forced, with B stored transposed, C through LDS or straight from the
+accumulators, the one-thread-per-output fallback), exact on integer
+inputs, within the bf16 tolerance on random ones, and at the attention
+shapes of a 2048-token, 32-head, d = 128 layer over every head's whole
+output."""
 import ctypes
 
 import numpy as np
@@ -127,6 +129,40 @@ def test_batched_128_tile(case, staged, monkeypatch):
     got, _ = run(A, B, None, 1.25, 0.0, trans_b, N)
     ref, den = oracle.gemm_batched(A, B, None, 1.25, 0.0, bf16=True, trans_b=trans_b)
     assert oracle.parity_error(got, ref, den) <= TOL["bf16"]
+
+
+# More 256 x 256 tiles than CUs: the persistent grid, whose workgroups take
+# every 256th tile and copy the next tile's first K steps while storing C.
+PERSIST = [  # (batch, M, N, K, trans_b)
+    (70, 300, 520, 72, True),     # 420 tiles, K tail, ragged M and N
+    (70, 300, 520, 128, False),
+    (70, 300, 520, 32, True),     # one K step per tile
+    (70, 300, 520, 64, False),    # two K steps per tile
+    (130, 256, 512, 96, True),    # 260 tiles: four workgroups take two tiles
+    (80, 264, 264, 200, False),   # 320 tiles, K tail
+]
+
+
+@pytest.mark.parametrize("case", PERSIST, ids=lambda c: "%dx%dx%dx%d_%s" % (c[:4] + ("bt" if c[4] else "bn",)))
+def test_batched_persistent(case, monkeypatch):
+    """Exact on integers with beta 0.5 (C read back in every tile's
+    epilogue), and on normal draws bit-identical to one workgroup per tile
+    (MGEMM_BATCHED_PERSIST=0): each tile's sums are formed in the same order
+    either way."""
+    batch, M, N, K, trans_b = case
+    A, B, C = make(batch, M, N, K, trans_b, "i:4", "i:4", 0.5, seed=batch * 100 + K + 2)
+    got, name = run(A, B, C, 1.0, 0.5, trans_b, N)
+    assert name == "bf16_q4_256x256x32_batched" + ("_bt" if trans_b else "") + "_persist", name
+    ref, _ = oracle.gemm_batched(A, B, C, 1.0, 0.5, bf16=True, trans_b=trans_b)
+    assert np.array_equal(got.astype(np.float64), ref)
+    A, B, _ = make(batch, M, N, K, trans_b, "n:1", "n:0.1", 0.0, seed=9 + K)
+    got, _ = run(A, B, None, 1.25, 0.0, trans_b, N)
+    ref, den = oracle.gemm_batched(A, B, None, 1.25, 0.0, bf16=True, trans_b=trans_b)
+    assert oracle.parity_error(got, ref, den) <= TOL["bf16"]
+    monkeypatch.setenv("MGEMM_BATCHED_PERSIST", "0")
+    one, name = run(A, B, None, 1.25, 0.0, trans_b, N)
+    assert name == "bf16_q4_256x256x32_batched" + ("_bt" if trans_b else ""), name
+    assert np.array_equal(got.view(np.uint32), one.view(np.uint32))
 
 
 @pytest.mark.parametrize("trans_b", [True, False], ids=["qk", "pv"])
