@@ -432,7 +432,8 @@ __device__ __forceinline__ void store_c_tile_lds128(const f32x16 (&acc)[MI][4], 
 // A's.  STAGED (128 x 128 only): the epilogue goes through LDS
 // (store_c_tile_lds, whole 256-byte row segments per store) instead of
 // 16-byte stores straight from the accumulators.
-template <int BM, int BN, bool KTAIL, bool EPI, bool TRANSB = false, bool STAGED = false>
+template <int BM, int BN, bool KTAIL, bool EPI, bool TRANSB = false, bool STAGED = false,
+          int S = 2>
 __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, int K, float alpha,
                                                                 float beta,
                                                                 const uint16_t *__restrict__ A,
@@ -441,8 +442,9 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
                                                                 int tiles_n, Epi epi,
                                                                 Batch batch) {
     using T = Tile<BM, BN>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][T::A_STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][T::B_STAGE];
+    static_assert(S >= 2, "at least two stages");
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[S][T::A_STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b[S][T::B_STAGE];
 
     // XCD-aware order over the tiles of all items (one item: the plain GEMM)
     int tm, tn;
@@ -578,28 +580,39 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
     const int ktiles = (K + kBK - 1) / kBK;
-    issue_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    constexpr int kCopies = T::A_LOADS + T::B_LOADS;
+    // vmcnt <= copies of S - 2 tiles and lgkmcnt == 0
+    constexpr int kWaitAhead = ((S - 2) * kCopies & 15) | (7 << 4) | (((S - 2) * kCopies >> 4) << 14);
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)
+        if (u == 0 || u < ktiles) issue_tile(u * kBK, u);
+    if (S == 2 || ktiles < S - 1)
+        __builtin_amdgcn_s_waitcnt(0);
+    else
+        __builtin_amdgcn_s_waitcnt(kWaitAhead);
     __syncthreads();
 
-    // Software pipeline of one K step (tile t in stage t % 2):
-    //   issue direct loads of tile t+1 into the other stage
+    // Software pipeline of one K step (tile t in stage t % S):
+    //   issue direct loads of tile t+S-1 into the stage tile t-1 used
     //   sub-steps 0..2: read fragments of sub-step s+1, 16 MFMAs of sub-step s
-    //   sub-step 3:     wait for own loads + barrier (the current stage is
-    //                   then no longer read and tile t+1 is complete), read
-    //                   tile t+1's sub-step-0 fragments, 16 MFMAs of sub-step 3
-    // Past the last tile the "next" tile lies beyond K, so its loads are all
-    // out of range and only write zeros into the idle stage.  Scheduling
-    // barriers keep each sub-step's fragment reads (and the step's global
-    // loads) interleaved with its MFMAs.
+    //   sub-step 3:     wait for own loads of tile t+1 + barrier (the
+    //                   current stage is then no longer read and tile t+1 is
+    //                   complete), read tile t+1's sub-step-0 fragments, 16
+    //                   MFMAs of sub-step 3
+    // With two stages, past the last tile the "next" tile lies beyond K, so
+    // its loads are all out of range and only write zeros into the idle
+    // stage; with more, tiles past K are not copied, and the last S - 1
+    // steps wait for every copy.  Scheduling barriers keep each sub-step's
+    // fragment reads (and the step's global loads) interleaved with its
+    // MFMAs.
     bf16x8 fa[2][T::MI];
     s16x8 fb[2][T::NI];
     read_frags(0, 0, fa[0], fb[0]);
     constexpr int kMfma = T::MI * T::NI;
-    constexpr int kCopies = T::A_LOADS + T::B_LOADS;
     for (int t = 0; t < ktiles; ++t) {
-        const int cur = t & 1;
-        const TileCopy copy = tile_copy((t + 1) * kBK, cur ^ 1);
+        const int cur = t % S;
+        const bool ahead = t + S - 1 < ktiles;  // tile t + S - 1 exists
+        const TileCopy copy = tile_copy((t + S - 1) * kBK, (t + S - 1) % S);
 #pragma unroll
         for (int s = 0; s < kBK / 16; ++s) {
             const int f = s & 1;
@@ -623,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
                         const int rq = q * kReadsPerSlot + u;
                         if (rq < kReads) read_one(cur, s + 1, rq, fa[f ^ 1], fb[f ^ 1]);
                     }
-                    if (s == 0) {
+                    if (s == 0 && (S == 2 || ahead)) {
 #pragma unroll
                         for (int u = 0; u < kCopiesPerSlot; ++u) {
                             const int cq = q * kCopiesPerSlot + u;
@@ -632,14 +645,19 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
                     }
                 } else {
                     if (q == kHalf - 1) {
-                        __builtin_amdgcn_s_waitcnt(0);  // own copies of tile t+1 landed
-                        __syncthreads();                // ... and everyone else's
+                        // own copies of tile t+1 landed ...
+                        if (S == 2 || !ahead)
+                            __builtin_amdgcn_s_waitcnt(0);
+                        else
+                            __builtin_amdgcn_s_waitcnt(kWaitAhead);
+                        __syncthreads();  // ... and everyone else's
                     }
                     if (q >= kHalf) {
 #pragma unroll
                         for (int u = 0; u < kReadsPerLateSlot; ++u) {
                             const int rq = (q - kHalf) * kReadsPerLateSlot + u;
-                            if (rq < kReads) read_one(cur ^ 1, 0, rq, fa[f ^ 1], fb[f ^ 1]);
+                            if (rq < kReads)
+                                read_one((t + 1) % S, 0, rq, fa[f ^ 1], fb[f ^ 1]);
                         }
                     }
                 }
@@ -653,9 +671,12 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_mfma_kernel(int M, int N, in
         make_rsrc(C + static_cast<size_t>(m0) * N + n0,
                   (static_cast<long long>(M - m0) * N - n0) * 4);
     if constexpr (STAGED) {
-        // every wave's last reads are done before any wave reuses a stage:
-        // waves 0 and 1 stage through the two A stages, 2 and 3 the B stages
-        static_assert(BM == 128 && BN == 128, "16 KB stages, one per wave");
+        // every wave's last reads are done before any wave reuses a stage
+        // (and, the last step having waited for every copy, no copy is in
+        // flight): waves 0 and 1 stage through A stages 0 and 1, 2 and 3
+        // through B stages 0 and 1
+        static_assert(T::NI == 2 && T::A_STAGE * 2 >= 16384 && T::B_STAGE * 2 >= 16384,
+                      "64-column wave tiles, 16 KB stages");
         __syncthreads();
         float *region = reinterpret_cast<float *>(wave < 2 ? &lds_a[wave][0] : &lds_b[wave - 2][0]);
         store_c_tile_lds<T::MI, T::NI, kStoreC, kSystemScope, EPI>(
@@ -2349,6 +2370,31 @@ hipError_t launch_cfg(int M, int N, int K, float alpha, float beta, const uint16
     return hipGetLastError();
 }
 
+// Batched calls with B as K x N and no fused epilogue on S LDS stages (copies
+// S - 1 K steps ahead), C stored straight from the accumulators or through
+// LDS (staged).
+template <int BM, int BN, int S>
+hipError_t launch_deep(int M, int N, int K, float alpha, float beta, const uint16_t *A,
+                       const uint16_t *B, float *C, hipStream_t stream, const Batch &batch,
+                       bool staged) {
+    const long long tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const long long tiles = tiles_m * tiles_n * batch.items;
+    if (tiles > 0x7fffffffLL || batch.items < 1) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(tiles)), block(kThreads);
+    const int tm = static_cast<int>(tiles_m), tn = static_cast<int>(tiles_n);
+    auto go = [&](auto kt, auto st) {
+        bf16_mfma_kernel<BM, BN, decltype(kt)::value, false, false, decltype(st)::value, S>
+            <<<grid, block, 0, stream>>>(M, N, K, alpha, beta, A, B, C, tm, tn, kNoEpi, batch);
+    };
+    auto with_st = [&](auto kt) {
+        if (staged) go(kt, std::true_type());
+        else go(kt, std::false_type());
+    };
+    if (K % kBK != 0) with_st(std::true_type());
+    else with_st(std::false_type());
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int S>
 hipError_t launch_pp(int M, int N, int K, float alpha, float beta, const uint16_t *A,
                      const uint16_t *B, float *C, const PPSplit *split, const Epi &epi,
@@ -2474,8 +2520,17 @@ int fp8_split_tiles(int M, int N, int K, int num_cus, int bk) {
 
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
                                const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
-                               bool trans_b, hipStream_t stream, bool staged, int persist_grid) {
+                               bool trans_b, hipStream_t stream, bool staged, int persist_grid,
+                               int stages) {
     if (persist_grid != 0 && cfg != 0) return hipErrorInvalidValue;
+    if (stages != 2) {
+        if (trans_b) return hipErrorInvalidValue;
+        if (cfg == 3 && stages == 4)
+            return launch_deep<128, 128, 4>(M, N, K, alpha, beta, A, B, C, stream, batch, staged);
+        if (cfg == 1 && stages == 3)
+            return launch_deep<256, 128, 3>(M, N, K, alpha, beta, A, B, C, stream, batch, staged);
+        return hipErrorInvalidValue;
+    }
     switch (cfg) {
         case 0:
             return launch_q4<false>(M, N, K, alpha, beta, A, B, C, nullptr, kNoEpi, stream, batch,

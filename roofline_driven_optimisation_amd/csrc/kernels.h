@@ -112,13 +112,15 @@ hipError_t launch_bf16_mfma(int cfg, int M, int N, int K, float alpha, float bet
 // (the four-wave kernel on 16 x 16 MFMAs), each with B as K x N or stored
 // transposed, N x K (trans_b); `staged` (cfg 3 only) stores C through LDS;
 // `persist_grid` (cfg 0 only, a multiple of 8, 0 for none) runs that many
-// workgroups, each over every grid-th tile, when there are more tiles.
-// The same shape requirements as launch_bf16_mfma, for every item (strides
-// keep each item 16-byte aligned).
+// workgroups, each over every grid-th tile, when there are more tiles;
+// `stages` other than 2 (B as K x N only): 128 x 128 tiles (cfg 3) on 4 LDS
+// stages or 256 x 128 tiles (cfg 1) on 3, copies that many K steps less one
+// ahead.  The same shape requirements as launch_bf16_mfma, for every item
+// (strides keep each item 16-byte aligned).
 hipError_t launch_bf16_batched(int cfg, int M, int N, int K, float alpha, float beta,
                                const uint16_t *A, const uint16_t *B, float *C, const Batch &batch,
                                bool trans_b, hipStream_t stream, bool staged = false,
-                               int persist_grid = 0);
+                               int persist_grid = 0, int stages = 2);
 // 8-bit float GEMM, C = alpha A B^T + beta C with B stored N x K: fmt 0
 // E4M3, 1 E5M2 (both operands).  Needs K % 16 == 0, 16-byte aligned A and
 // B, K <= 2^21 and N <= 2^20.  `wide`: the 128-deep K step kernel, else the

@@ -131,6 +131,37 @@ def test_batched_128_tile(case, staged, monkeypatch):
     assert oracle.parity_error(got, ref, den) <= TOL["bf16"]
 
 
+# O = P V shapes (N <= 128, B as K x N) on deeper pipelines
+# (MGEMM_BATCHED_DEEP): 128 x 128 tiles on four LDS stages (1) and 256 x 128
+# tiles on three (2), copies up to three K steps ahead, C either way.
+DEEP = [  # (batch, M, N, K)
+    (4, 300, 128, 264),    # five K steps, the last a tail
+    (2, 264, 120, 72),     # N < 128, fewer K steps than stages
+    (3, 520, 128, 64),     # one K step
+    (5, 256, 128, 1000),   # 16 K steps, a tail
+]
+
+
+@pytest.mark.parametrize("staged", [False, True], ids=["direct", "lds"])
+@pytest.mark.parametrize("deep", [1, 2])
+@pytest.mark.parametrize("case", DEEP, ids=lambda c: "%dx%dx%dx%d" % c)
+def test_batched_deep(case, deep, staged, monkeypatch):
+    batch, M, N, K = case
+    monkeypatch.setenv("MGEMM_BATCHED_DEEP", str(deep))
+    monkeypatch.setenv("MGEMM_BATCHED_STAGED", "1" if staged else "0")
+    A, B, C = make(batch, M, N, K, False, "i:4", "i:4", 0.5, seed=batch * 100 + K + 3)
+    got, name = run(A, B, C, 1.0, 0.5, False, N)
+    want = ("bf16_mfma_128x128x64_s4_batched" if deep == 1 else
+            "bf16_mfma_256x128x64_s3_batched") + ("" if staged else "_direct")
+    assert name == want, name
+    ref, _ = oracle.gemm_batched(A, B, C, 1.0, 0.5, bf16=True)
+    assert np.array_equal(got.astype(np.float64), ref)
+    A, B, _ = make(batch, M, N, K, False, "n:1", "n:0.1", 0.0, seed=10 + K)
+    got, _ = run(A, B, None, 1.25, 0.0, False, N)
+    ref, den = oracle.gemm_batched(A, B, None, 1.25, 0.0, bf16=True)
+    assert oracle.parity_error(got, ref, den) <= TOL["bf16"]
+
+
 # More 256 x 256 tiles than CUs: the persistent grid, whose workgroups take
 # every 256th tile and copy the next tile's first K steps while storing C.
 PERSIST = [  # (batch, M, N, K, trans_b)
