@@ -1,4 +1,5 @@
-"""The library under HIP graph capture (torch.cuda.graph).
+"""The library under HIP graph capture (torch.cuda.graph), for the plain,
+decode-shaped, 8-bit float and batched GEMMs.
 
 Under capture the library allocates nothing, runs no placement probe and
 never uses the ping-pong kernel's split tail (its flag epochs would be stale
@@ -115,3 +116,40 @@ def test_fp8_split_shape_unsplit_under_capture(torch):
         assert "splitk" in binding.last_kernel(), binding.last_kernel()
         torch.cuda.synchronize()
         assert np.array_equal(D.cpu().numpy().astype(np.float64), ref), r
+
+
+@pytest.mark.parametrize("shape", [(70, 300, 520, 72, True), (64, 1024, 128, 136, False)],
+                         ids=["qk_persistent", "pv_three_stage"])
+def test_batched_under_capture(torch, shape):
+    """The batched GEMM's persistent grid (more 256 x 256 tiles than CUs)
+    and the three-stage 256 x 128 kernel (tiles that fill every CU) captured
+    into a graph: every replay, with eager batched calls of another shape in
+    between, equals the oracle exactly on integers."""
+    from roofline_driven_optimisation_amd.inputs import f32_to_bf16_bits
+    batch, M, N, K, trans_b = shape
+    rng = np.random.default_rng(84)
+    a = f32_to_bf16_bits(rng.integers(-4, 5, (batch, M, K)).astype(np.float32))
+    b = f32_to_bf16_bits(rng.integers(-4, 5, (batch, N, K) if trans_b else (batch, K, N))
+                         .astype(np.float32))
+    c0 = rng.integers(-8, 9, (batch, M, N)).astype(np.float32)
+    ref, _ = oracle.gemm_batched(a, b, c0, 1.0, 0.5, bf16=True, trans_b=trans_b)
+    A = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    B = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    C0 = torch.from_numpy(c0).cuda()
+    C = C0.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.gemm_bf16_batched(A, B, C, 1.0, 0.5, trans_b=trans_b)
+    name = binding.last_kernel()
+    assert name.endswith("_persist") if trans_b else "_s3_" in name, name
+    oa = torch.ones(3, 264, 64, dtype=torch.bfloat16, device="cuda")
+    ob = torch.ones(3, 64, 256, dtype=torch.bfloat16, device="cuda")
+    oc = torch.zeros(3, 264, 256, device="cuda")
+    for r in range(4):
+        C.copy_(C0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref), (name, r)
+        binding.gemm_bf16_batched(oa, ob, oc, 1.0, 0.0)
+        torch.cuda.synchronize()
