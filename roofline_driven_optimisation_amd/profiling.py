@@ -198,7 +198,7 @@ def mfma_rows(path: str, last: int = 0):
 
 
 def counter_runs(paths, labels, last: int = 8,
-                 kernels=("bf16_q4", "bf16_q16", "fp8_q4", "fp8_wide")):
+                 kernels=("bf16_q4", "bf16_q16", "bf16_mfma", "fp8_q4", "fp8_wide")):
     """Median counter values per workload from one or more --pmc passes of
     the same bench command: each pass's dispatches are split into runs of
     consecutive dispatches of one kernel and launch shape (one run per
